@@ -1,0 +1,170 @@
+/*
+ * s4kv -- int4 KIVI paged KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * The method: the S4 KV product page ("int4 KV-Cache-Kompression fuer vLLM",
+ * header paragraph and "Funktionsweise" step 1) stores the paged-attention KV
+ * cache in int4 instead of fp16, KIVI style and asymmetric: KEY quantized per
+ * channel, VALUE per token; supported models have head_dim 128 and standard
+ * attention, and anything else is refused up front ("fail-fast", sections
+ * "Highlights" and "FAQ"). Pages of 16 tokens reached through a page table
+ * follow the PagedAttention explainers (gyaansetu.com "KV-Cache und
+ * PagedAttention", section "Wie PagedAttention das loest").
+ *
+ * This library implements
+ *   - s4kv_quantize_append: append new K/V tokens of each sequence; a page is
+ *     quantized to int4 when its 16th token arrives, earlier tokens of the
+ *     page wait in an fp16 residual tail;
+ *   - s4kv_paged_decode: one decode step of attention for every sequence over
+ *     its int4 pages plus its fp16 tail (GQA, split over pages, cross-split
+ *     softmax reduction).
+ *
+ * Quantizer (per group of fp16 values x): zero z = min(x) as fp16, scale
+ * s = fp16((max - min) / 15) computed in fp32, code = clamp(rint_even((x - z)
+ * / s), 0, 15) in IEEE fp32 with the stored fp16 s and z, codes 0 and scale
+ * +0 when s is 0, -0 stored as +0. Dequantized value: code * s + z.
+ *
+ * Conventions for every call:
+ *   - Pointers named "device" are HIP device pointers; the caller allocates
+ *     and owns all memory, including the decode workspace. The library never
+ *     allocates, holds no state between calls, and is safe to call from
+ *     several host threads.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; no call synchronizes the host.
+ *   - Shapes are checked on the host before anything is launched; a bad shape
+ *     or argument returns an error status and enqueues nothing. Device-side
+ *     preconditions (listed per call) are not checked in the kernels.
+ *
+ * Page format (one "chunk" per physical page and KV head; the pool is
+ * uint8 pages[num_pages][num_kv_heads][S4KV_CHUNK_STRIDE]):
+ *   offset    0: K codes, 1024 B      offset 1024: V codes, 1024 B
+ *   offset 2048: K scale fp16[128]    offset 2304: K zero fp16[128]   (per channel)
+ *   offset 2560: V scale fp16[16]     offset 2592: V zero fp16[16]    (per token)
+ *   offset 2624: 64 B padding (written as zero)
+ * Codes are 4-bit, two per byte, low nibble first. Inside the 1024-B K block,
+ * byte 16*l + 4*m + k/2 (nibble k = 0..7 of dword m = 0..3 of 16-byte lane
+ * block l = 16*g + t) holds the K code of token t, channel
+ * d = 32*m + 8*g + 2*(k%4) + k/4. Inside the V block, lane block
+ * l = 16*g + r, dword m, nibble k holds the V code of token
+ * t = 4*g + 2*(k%2) + k/4, channel d = 16*(2*m + (k%4)/2) + r.
+ * (This order lets the decode kernel feed each 16-byte load straight into
+ * matrix-core operands.)
+ */
+#ifndef S4KV_H_
+#define S4KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define S4KV_HEAD_DIM 128
+#define S4KV_PAGE_SIZE 16
+#define S4KV_CHUNK_BYTES 2624 /* bytes of a chunk that carry data */
+#define S4KV_CHUNK_STRIDE 2688 /* chunk stride in the pool (128-byte multiple) */
+#define S4KV_MAX_GROUP 16 /* largest supported query heads per KV head */
+
+typedef enum s4kv_status {
+  S4KV_OK = 0,
+  S4KV_ERR_INVALID_ARG = 1, /* null pointer, negative or zero count, bad bound */
+  S4KV_ERR_UNSUPPORTED = 2, /* head_dim != 128, page_size != 16, Hq % Hkv != 0,
+                               Hq / Hkv > 16: the model is refused */
+  S4KV_ERR_WORKSPACE = 3,   /* decode workspace smaller than required */
+  S4KV_ERR_HIP = 4          /* a HIP launch failed (hipGetLastError) */
+} s4kv_status;
+
+typedef struct s4kv_shape {
+  int32_t num_seqs;          /* B: sequences in the batch (rows of block table) */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv; Hq must be a multiple, Hq / Hkv <= 16 */
+  int32_t head_dim;          /* must be 128 */
+  int32_t page_size;         /* must be 16 */
+  int32_t num_pages;         /* physical pages in this layer's pool */
+  int32_t max_pages_per_seq; /* row length of the block table */
+} s4kv_shape;
+
+/* Check a shape without touching the GPU (S4 KV page, "FAQ": unsupported
+ * models are refused at start instead of producing wrong output).
+ * Returns S4KV_OK, S4KV_ERR_INVALID_ARG (null, counts < 1) or
+ * S4KV_ERR_UNSUPPORTED. */
+s4kv_status s4kv_validate(const s4kv_shape* shape);
+
+/* Human-readable name of a status. Never NULL; static storage. */
+const char* s4kv_status_string(s4kv_status status);
+
+/* Bytes the caller must allocate for one layer's page pool:
+ * num_pages * num_kv_heads * S4KV_CHUNK_STRIDE. 0 if the shape is invalid. */
+size_t s4kv_pool_bytes(const s4kv_shape* shape);
+
+/* Bytes of ONE fp16 residual-tail buffer (K or V) for one layer:
+ * num_seqs * num_kv_heads * 16 * 128 * 2, layout fp16 [B][Hkv][16][128]
+ * indexed by the token's position modulo 16. 0 if the shape is invalid. */
+size_t s4kv_tail_bytes(const s4kv_shape* shape);
+
+/* Append new tokens to every sequence of one layer.
+ *
+ * Args (device pointers unless noted):
+ *   k, v         fp16 [total_new][Hkv][128], contiguous; the new tokens of
+ *                sequence b are rows cu_new[b] .. cu_new[b+1]-1, in order.
+ *   cu_new       int32 [B+1], cu_new[0] = 0, non-decreasing.
+ *   slot         int32 [B]: tokens already cached for sequence b, i.e. the
+ *                position of its first new token.
+ *   max_new      host int: an upper bound on cu_new[b+1]-cu_new[b] for every
+ *                b (1 for a decode step). It sizes the launch only.
+ *   block_table  int32 [B][max_pages_per_seq]: physical page of each logical
+ *                page of each sequence.
+ *   pages        the layer's pool (s4kv_pool_bytes); written.
+ *   tail_k/v     the layer's fp16 tails (s4kv_tail_bytes each); read and written.
+ * Effect: for every page that becomes full, its 16 tokens (older ones from
+ * the tail, new ones from k/v) are quantized and written to the chunk
+ * block_table[b][page] of each KV head; new tokens of a page that stays
+ * partial are written to the tail at (position % 16).
+ * Device preconditions: new tokens per sequence <= max_new; slot[b] + new
+ * tokens <= 16 * max_pages_per_seq; block ids in [0, num_pages); the tail of
+ * b holds its tokens 16*floor(slot/16) .. slot-1 (as left by earlier calls);
+ * no two sequences write the same physical page in one call; k and v finite.
+ * Returns S4KV_OK or an error before any launch; S4KV_ERR_HIP if the launch
+ * fails. */
+s4kv_status s4kv_quantize_append(const s4kv_shape* shape, const void* k, const void* v,
+                                 const int32_t* cu_new, const int32_t* slot, int32_t max_new,
+                                 const int32_t* block_table, void* pages, void* tail_k,
+                                 void* tail_v, void* stream);
+
+/* Bytes of device workspace s4kv_paged_decode needs for this shape and a
+ * context bound max_ctx (host int). 0 if the shape is invalid or max_ctx < 1. */
+size_t s4kv_decode_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx);
+
+/* One decode step of attention for every sequence of one layer.
+ *
+ * For sequence b and query head j (KV head h = j / (Hq/Hkv)):
+ *   O[b][j] = sum_t softmax_t(sm_scale * q[b][j] . k_t) v_t over the ctx_lens[b]
+ * cached tokens, where k_t, v_t are the dequantized int4 values for tokens in
+ * full pages and the fp16 tail values for the last ctx_lens[b] % 16 tokens.
+ *
+ * Args (device pointers unless noted):
+ *   q            fp16 [B][Hq][128].
+ *   pages, tail_k, tail_v  the layer's cache (read only).
+ *   block_table  int32 [B][max_pages_per_seq].
+ *   ctx_lens     int32 [B]: cached tokens per sequence (after any append).
+ *   max_ctx      host int >= every ctx_lens[b]; sizes the launch and workspace.
+ *   sm_scale     host float, logit scale (1/sqrt(128) for standard attention).
+ *   out          fp16 [B][Hq][128]; written.
+ *   workspace    device scratch of at least s4kv_decode_workspace_bytes
+ *                (caller-owned; contents on entry do not matter).
+ * Device preconditions: 1 <= ctx_lens[b] <= max_ctx and <= 16 *
+ * max_pages_per_seq; block ids of full pages in [0, num_pages). A sequence
+ * with ctx_lens[b] <= 0 gets an all-zero output.
+ * Returns S4KV_OK; S4KV_ERR_INVALID_ARG / S4KV_ERR_UNSUPPORTED /
+ * S4KV_ERR_WORKSPACE before any launch; S4KV_ERR_HIP if a launch fails. */
+s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void* pages,
+                              const void* tail_k, const void* tail_v,
+                              const int32_t* block_table, const int32_t* ctx_lens,
+                              int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S4KV_H_ */

@@ -1,0 +1,56 @@
+"""Device buffers of one layer's int4 KIVI cache, allocated with torch.
+
+A convenience over the C ABI for Python callers: it owns the page pool, the
+two fp16 tails and the decode workspace of one layer and forwards every call
+to libs4kv.so. The block table and context lengths stay with the caller (they
+are shared by all layers of a model).
+"""
+
+import math
+
+import torch
+
+from . import s4kv
+
+
+class LayerCache:
+    def __init__(self, shape, device="cuda"):
+        if s4kv.s4kv_validate(shape) != s4kv.S4KV_OK:
+            raise s4kv.S4KVError(s4kv.s4kv_validate(shape), "LayerCache")
+        self.shape = shape
+        self.device = torch.device(device)
+        self.pages = torch.zeros(s4kv.s4kv_pool_bytes(shape), dtype=torch.uint8, device=self.device)
+        n_tail = s4kv.s4kv_tail_bytes(shape) // 2
+        self.tail_k = torch.zeros(n_tail, dtype=torch.float16, device=self.device)
+        self.tail_v = torch.zeros(n_tail, dtype=torch.float16, device=self.device)
+        self._ws = None
+        self._ws_ctx = 0
+
+    def workspace(self, max_ctx):
+        need = s4kv.s4kv_decode_workspace_bytes(self.shape, max_ctx)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def append(self, k, v, cu_new, slot, max_new, block_table, stream=None):
+        s4kv.s4kv_quantize_append(self.shape, k, v, cu_new, slot, max_new, block_table,
+                                  self.pages, self.tail_k, self.tail_v, stream)
+
+    def decode(self, q, block_table, ctx_lens, max_ctx, sm_scale=None, out=None, stream=None):
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(self.shape.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        s4kv.s4kv_paged_decode(self.shape, q, self.pages, self.tail_k, self.tail_v, block_table,
+                               ctx_lens, max_ctx, sm_scale, out, self.workspace(max_ctx), stream)
+        return out
+
+    def chunk_view(self):
+        """uint8 [num_pages, Hkv, CHUNK_STRIDE] view of the pool."""
+        return self.pages.view(self.shape.num_pages, self.shape.num_kv_heads, s4kv.CHUNK_STRIDE)
+
+    def tails(self):
+        """(tail_k, tail_v) as fp16 [B, Hkv, 16, 128] views."""
+        s = self.shape
+        dims = (s.num_seqs, s.num_kv_heads, s.page_size, s.head_dim)
+        return self.tail_k.view(*dims), self.tail_v.view(*dims)

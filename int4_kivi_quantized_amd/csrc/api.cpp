@@ -1,0 +1,97 @@
+// C ABI of the s4kv library: host-side validation and dispatch.
+//
+// Fail-fast validation follows the S4 KV product page ("Highlights", "FAQ"):
+// only head_dim 128 with standard attention is supported, and anything else is
+// refused before any work is done rather than producing wrong output.
+#include <hip/hip_runtime_api.h>
+
+#include "internal.h"
+
+namespace {
+
+s4kv_status check_shape(const s4kv_shape* s) {
+  if (s == nullptr) return S4KV_ERR_INVALID_ARG;
+  if (s->num_seqs < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->num_pages < 1 ||
+      s->max_pages_per_seq < 1)
+    return S4KV_ERR_INVALID_ARG;
+  if (s->head_dim != S4KV_HEAD_DIM || s->page_size != S4KV_PAGE_SIZE) return S4KV_ERR_UNSUPPORTED;
+  if (s->num_q_heads % s->num_kv_heads != 0) return S4KV_ERR_UNSUPPORTED;
+  if (s->num_q_heads / s->num_kv_heads > S4KV_MAX_GROUP) return S4KV_ERR_UNSUPPORTED;
+  // launch-grid limits (y and z dimensions)
+  if (s->num_kv_heads > 65535 || s->num_seqs > 65535 || s->num_q_heads > 65535)
+    return S4KV_ERR_UNSUPPORTED;
+  // block-table products must fit in int32 page counts
+  if ((int64_t)s->max_pages_per_seq * S4KV_PAGE_SIZE > INT32_MAX) return S4KV_ERR_INVALID_ARG;
+  return S4KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+s4kv_status s4kv_validate(const s4kv_shape* shape) { return check_shape(shape); }
+
+const char* s4kv_status_string(s4kv_status status) {
+  switch (status) {
+    case S4KV_OK: return "ok";
+    case S4KV_ERR_INVALID_ARG: return "invalid argument";
+    case S4KV_ERR_UNSUPPORTED: return "unsupported shape (needs head_dim 128, page 16, Hq % Hkv == 0, Hq/Hkv <= 16)";
+    case S4KV_ERR_WORKSPACE: return "workspace too small";
+    case S4KV_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t s4kv_pool_bytes(const s4kv_shape* shape) {
+  if (check_shape(shape) != S4KV_OK) return 0;
+  return (size_t)shape->num_pages * shape->num_kv_heads * S4KV_CHUNK_STRIDE;
+}
+
+size_t s4kv_tail_bytes(const s4kv_shape* shape) {
+  if (check_shape(shape) != S4KV_OK) return 0;
+  return (size_t)shape->num_seqs * shape->num_kv_heads * S4KV_PAGE_SIZE * S4KV_HEAD_DIM * 2;
+}
+
+s4kv_status s4kv_quantize_append(const s4kv_shape* shape, const void* k, const void* v,
+                                 const int32_t* cu_new, const int32_t* slot, int32_t max_new,
+                                 const int32_t* block_table, void* pages, void* tail_k,
+                                 void* tail_v, void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (max_new < 0) return S4KV_ERR_INVALID_ARG;
+  if (!k || !v || !cu_new || !slot || !block_table || !pages || !tail_k || !tail_v)
+    return S4KV_ERR_INVALID_ARG;
+  if (max_new == 0) return S4KV_OK;
+  if ((int64_t)max_new > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
+    return S4KV_ERR_INVALID_ARG;
+  const hipError_t e = s4kv::launch_quantize_append(*shape, k, v, cu_new, slot, max_new,
+                                                    block_table, pages, tail_k, tail_v,
+                                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
+size_t s4kv_decode_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx) {
+  if (check_shape(shape) != S4KV_OK || max_ctx < 1) return 0;
+  return s4kv::workspace_bytes(*shape, s4kv::plan_splits(*shape, max_ctx));
+}
+
+s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void* pages,
+                              const void* tail_k, const void* tail_v,
+                              const int32_t* block_table, const int32_t* ctx_lens,
+                              int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
+    return S4KV_ERR_INVALID_ARG;
+  if (!q || !pages || !tail_k || !tail_v || !block_table || !ctx_lens || !out || !workspace)
+    return S4KV_ERR_INVALID_ARG;
+  const s4kv::SplitPlan plan = s4kv::plan_splits(*shape, max_ctx);
+  if (workspace_bytes < s4kv::workspace_bytes(*shape, plan)) return S4KV_ERR_WORKSPACE;
+  const hipError_t e = s4kv::launch_paged_decode(*shape, plan, q, pages, tail_k, tail_v,
+                                                 block_table, ctx_lens, sm_scale, out, workspace,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal declarations shared by the C-ABI layer and the HIP translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "s4kv.h"
+
+namespace s4kv {
+
+constexpr int kHeadDim = S4KV_HEAD_DIM;
+constexpr int kPage = S4KV_PAGE_SIZE;
+constexpr int kChunkBytes = S4KV_CHUNK_BYTES;
+constexpr int kChunkStride = S4KV_CHUNK_STRIDE;
+constexpr int kMaxGroup = S4KV_MAX_GROUP;
+
+// Offsets inside a chunk (see s4kv.h, "Page format").
+constexpr int kOffKCodes = 0;
+constexpr int kOffVCodes = 1024;
+constexpr int kOffKScale = 2048;
+constexpr int kOffKZero = 2304;
+constexpr int kOffVScale = 2560;
+constexpr int kOffVZero = 2592;
+
+// Decode split plan: pages handled by one work-group, number of splits.
+struct SplitPlan {
+  int pages_per_split;
+  int max_splits;
+};
+SplitPlan plan_splits(const s4kv_shape& s, int32_t max_ctx);
+size_t workspace_bytes(const s4kv_shape& s, const SplitPlan& plan);
+
+hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void* v,
+                                  const int32_t* cu_new, const int32_t* slot, int32_t max_new,
+                                  const int32_t* block_table, void* pages, void* tail_k,
+                                  void* tail_v, hipStream_t stream);
+
+hipError_t launch_paged_decode(const s4kv_shape& s, const SplitPlan& plan, const void* q,
+                               const void* pages, const void* tail_k, const void* tail_v,
+                               const int32_t* block_table, const int32_t* ctx_lens,
+                               float sm_scale, void* out, void* workspace, hipStream_t stream);
+
+}  // namespace s4kv

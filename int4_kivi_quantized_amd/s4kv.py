@@ -1,0 +1,178 @@
+"""Thin Python binding of the s4kv C ABI (include/s4kv.h).
+
+Argument marshalling only: every step of quantization and attention runs in
+the HIP kernels of libs4kv.so. torch provides device memory and the current
+stream. There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+Function names are the C names; tensor arguments replace the raw pointers and
+are checked for dtype, device and contiguity before the call.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs4kv.so")
+
+HEAD_DIM = 128
+PAGE_SIZE = 16
+CHUNK_BYTES = 2624
+CHUNK_STRIDE = 2688
+MAX_GROUP = 16
+
+S4KV_OK = 0
+S4KV_ERR_INVALID_ARG = 1
+S4KV_ERR_UNSUPPORTED = 2
+S4KV_ERR_WORKSPACE = 3
+S4KV_ERR_HIP = 4
+
+
+class S4KVError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {s4kv_status_string(status)} (status {status})")
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+    ]
+
+
+@dataclass(frozen=True)
+class Shape:
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    num_pages: int
+    max_pages_per_seq: int
+    head_dim: int = HEAD_DIM
+    page_size: int = PAGE_SIZE
+
+    def c(self):
+        return _Shape(self.num_seqs, self.num_q_heads, self.num_kv_heads, self.head_dim,
+                      self.page_size, self.num_pages, self.max_pages_per_seq)
+
+
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load():
+    """Load libs4kv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m int4_kivi_quantized_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    SP = ctypes.POINTER(_Shape)
+    I32 = ctypes.c_int32
+    lib.s4kv_validate.argtypes = [SP]
+    lib.s4kv_validate.restype = ctypes.c_int
+    lib.s4kv_status_string.argtypes = [ctypes.c_int]
+    lib.s4kv_status_string.restype = ctypes.c_char_p
+    lib.s4kv_pool_bytes.argtypes = [SP]
+    lib.s4kv_pool_bytes.restype = ctypes.c_size_t
+    lib.s4kv_tail_bytes.argtypes = [SP]
+    lib.s4kv_tail_bytes.restype = ctypes.c_size_t
+    lib.s4kv_quantize_append.argtypes = [SP, P, P, P, P, I32, P, P, P, P, P]
+    lib.s4kv_quantize_append.restype = ctypes.c_int
+    lib.s4kv_decode_workspace_bytes.argtypes = [SP, I32]
+    lib.s4kv_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.s4kv_paged_decode.argtypes = [SP, P, P, P, P, P, P, I32, ctypes.c_float, P, P,
+                                      ctypes.c_size_t, P]
+    lib.s4kv_paged_decode.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+EXPORTED = (
+    "s4kv_validate", "s4kv_status_string", "s4kv_pool_bytes", "s4kv_tail_bytes",
+    "s4kv_quantize_append", "s4kv_decode_workspace_bytes", "s4kv_paged_decode",
+)
+
+
+def s4kv_status_string(status):
+    return load().s4kv_status_string(int(status)).decode()
+
+
+def s4kv_validate(shape):
+    return load().s4kv_validate(ctypes.byref(shape.c()))
+
+
+def s4kv_pool_bytes(shape):
+    return load().s4kv_pool_bytes(ctypes.byref(shape.c()))
+
+
+def s4kv_tail_bytes(shape):
+    return load().s4kv_tail_bytes(ctypes.byref(shape.c()))
+
+
+def s4kv_decode_workspace_bytes(shape, max_ctx):
+    return load().s4kv_decode_workspace_bytes(ctypes.byref(shape.c()), int(max_ctx))
+
+
+def _ptr(t, dtype, name, device=None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, where):
+    if status != S4KV_OK:
+        raise S4KVError(status, where)
+
+
+def s4kv_quantize_append(shape, k, v, cu_new, slot, max_new, block_table, pages, tail_k, tail_v,
+                         stream=None):
+    """Append new K/V tokens (fp16 [total_new, Hkv, 128]) to every sequence; see s4kv.h."""
+    import torch
+    st = load().s4kv_quantize_append(
+        ctypes.byref(shape.c()), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
+        _ptr(cu_new, torch.int32, "cu_new"), _ptr(slot, torch.int32, "slot"), int(max_new),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(pages, torch.uint8, "pages"),
+        _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),
+        _stream(stream))
+    _check(st, "s4kv_quantize_append")
+
+
+def s4kv_paged_decode(shape, q, pages, tail_k, tail_v, block_table, ctx_lens, max_ctx, sm_scale,
+                      out, workspace, stream=None):
+    """One decode step: out fp16 [B, Hq, 128] from q fp16 [B, Hq, 128]; see s4kv.h."""
+    import torch
+    st = load().s4kv_paged_decode(
+        ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(pages, torch.uint8, "pages"),
+        _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_lens, torch.int32, "ctx_lens"),
+        int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "s4kv_paged_decode")

@@ -1,0 +1,107 @@
+"""Build one layer's int4 cache on the GPU from a seeded workload, and compute
+oracle references for chosen sequences. Test infrastructure."""
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+import workload as W
+from int4_kivi_quantized_amd import Shape
+from int4_kivi_quantized_amd.cache import LayerCache
+
+
+class LayerCase:
+    """One layer of a workload: the GPU cache and everything needed to check it."""
+
+    def __init__(self, wl, layer=0, ctx_lens=None, extra_tokens=0, pool_seed_salt=None):
+        self.wl = wl
+        self.layer = layer
+        self.ctx = np.asarray(W.context_lengths(wl) if ctx_lens is None else ctx_lens, dtype=np.int64)
+        self.plan = W.plan_pages(wl, self.ctx, extra_tokens)
+        self.shape = Shape(wl.batch, wl.hq, wl.hkv, self.plan.num_pages, self.plan.max_pages)
+        self.cache = LayerCache(self.shape)
+        self.block_table = torch.from_numpy(self.plan.block_table).cuda()
+        self.ctx_gpu = torch.from_numpy(self.ctx.astype(np.int32)).cuda()
+        self.mult = W.k_channel_multipliers(wl, layer)
+        self.q = W.queries(wl, layer, "cuda")
+
+    # ------------------------------------------------------------- inputs
+    def seq_kv(self, b, device="cuda"):
+        return W.sequence_kv(self.wl, self.layer, b, int(self.ctx[b]), device, self.mult)
+
+    def prefill(self):
+        """Bulk prefill of every sequence through s4kv_quantize_append."""
+        wl = self.wl
+        alias = np.zeros(wl.batch, dtype=np.int64)
+        if len(self.plan.sharing):
+            share_pages = wl.shared_prefix // wl.page
+            pk, pv = W.prefix_kv(wl, self.layer, "cuda", self.mult)
+            pshape = Shape(1, wl.hq, wl.hkv, self.plan.num_pages, share_pages)
+            scratch = LayerCache(Shape(1, wl.hq, wl.hkv, 1, share_pages))   # tails only
+            bt = torch.from_numpy(self.plan.prefix_pages[None, :].copy()).cuda()
+            cu = torch.tensor([0, wl.shared_prefix], dtype=torch.int32, device="cuda")
+            sl = torch.zeros(1, dtype=torch.int32, device="cuda")
+            from int4_kivi_quantized_amd import s4kv
+            s4kv.s4kv_quantize_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
+                                      wl.shared_prefix, bt, self.cache.pages, scratch.tail_k,
+                                      scratch.tail_v)
+            for b in self.plan.sharing:
+                alias[b] = min(share_pages, int(self.ctx[b]) // wl.page)
+        ks, vs, starts, counts = [], [], [], []
+        for b in range(wl.batch):
+            k, v = self.seq_kv(b)
+            st = int(alias[b]) * wl.page
+            ks.append(k[st:])
+            vs.append(v[st:])
+            starts.append(st)
+            counts.append(int(self.ctx[b]) - st)
+        k_all = torch.cat(ks).contiguous()
+        v_all = torch.cat(vs).contiguous()
+        del ks, vs
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device="cuda")
+        sl = torch.tensor(np.asarray(starts, dtype=np.int32), device="cuda")
+        self.cache.append(k_all, v_all, cu, sl, max(counts), self.block_table)
+        torch.cuda.synchronize()
+
+    def decode(self, max_ctx=None):
+        if max_ctx is None:
+            max_ctx = int(self.ctx.max())
+        out = self.cache.decode(self.q, self.block_table, self.ctx_gpu, max_ctx)
+        torch.cuda.synchronize()
+        return out
+
+    # ------------------------------------------------------------- oracle side
+    def oracle_seq(self, b):
+        k, v = self.seq_kv(b)
+        return oracle.sequence_cache(k.cpu().numpy(), v.cpu().numpy())
+
+    def oracle_out(self, b, heads=None):
+        c = self.oracle_seq(b)
+        kh, vh = oracle.dequantized_sequence(c)
+        q = self.q[b].cpu().numpy()
+        if heads is not None:
+            # evaluate only the chosen query heads (each reads KV head j // G)
+            g = self.wl.group
+            out = np.zeros((self.wl.hq, self.wl.head_dim))
+            for j in heads:
+                h = j // g
+                out[j] = oracle.decode_attention(q[j:j + 1], kh[:, h:h + 1], vh[:, h:h + 1])[0]
+            return out
+        return oracle.decode_attention(q, kh, vh)
+
+    def gpu_chunks(self, b):
+        """uint8 [full_b, Hkv, STRIDE] of sequence b's full pages."""
+        full = int(self.ctx[b]) // self.wl.page
+        ids = self.plan.block_table[b, :full]
+        return self.cache.chunk_view()[torch.from_numpy(ids.astype(np.int64)).cuda()].cpu().numpy()
+
+    def gpu_tail(self, b):
+        tk, tv = self.cache.tails()
+        n = int(self.ctx[b]) % self.wl.page
+        return tk[b, :, :n].permute(1, 0, 2).cpu().numpy(), tv[b, :, :n].permute(1, 0, 2).cpu().numpy()
+
+
+def default_scale(d=128):
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,90 @@
+"""Reader (and, for checker self-tests, writer) of the library's page format,
+written from the format description in include/s4kv.h -- independent of both
+the HIP code and the oracle. Used to turn GPU page bytes into logical
+(token, channel) codes and fp16 scale/zero bit patterns.
+"""
+
+import numpy as np
+
+PAGE = 16
+D = 128
+CHUNK_BYTES = 2624
+CHUNK_STRIDE = 2688
+OFF_KC, OFF_VC, OFF_KS, OFF_KZ, OFF_VS, OFF_VZ = 0, 1024, 2048, 2304, 2560, 2592
+
+
+def _k_nibble_map():
+    """For each nibble index n = 2*byte + (high?1:0) in the K block: (token, channel)."""
+    tok = np.empty(2 * 1024, dtype=np.int64)
+    ch = np.empty(2 * 1024, dtype=np.int64)
+    for l in range(64):
+        t, g = l % 16, l // 16
+        for m in range(4):
+            for k in range(8):
+                byte = 16 * l + 4 * m + k // 2
+                n = 2 * byte + (k % 2)
+                tok[n] = t
+                ch[n] = 32 * m + 8 * g + 2 * (k % 4) + k // 4
+    return tok, ch
+
+
+def _v_nibble_map():
+    tok = np.empty(2 * 1024, dtype=np.int64)
+    ch = np.empty(2 * 1024, dtype=np.int64)
+    for l in range(64):
+        r, g = l % 16, l // 16
+        for m in range(4):
+            for k in range(8):
+                byte = 16 * l + 4 * m + k // 2
+                n = 2 * byte + (k % 2)
+                tok[n] = 4 * g + 2 * (k % 2) + k // 4
+                ch[n] = 16 * (2 * m + (k % 4) // 2) + r
+    return tok, ch
+
+
+K_TOK, K_CH = _k_nibble_map()
+V_TOK, V_CH = _v_nibble_map()
+
+
+def _nibbles(block):
+    """uint8 [..., 1024] -> uint8 [..., 2048] (low nibble first)."""
+    lo = block & 0x0F
+    hi = block >> 4
+    return np.stack([lo, hi], axis=-1).reshape(*block.shape[:-1], 2048)
+
+
+def read_chunks(raw):
+    """raw: uint8 [..., CHUNK_STRIDE] -> dict of logical arrays.
+
+    ck, cv: uint8 [..., 16, 128] (token, channel); sk, zk: uint16 bit patterns
+    [..., 128]; sv, zv: uint16 [..., 16]; pad: uint8 [..., 64].
+    """
+    raw = np.asarray(raw, dtype=np.uint8)
+    lead = raw.shape[:-1]
+    kn = _nibbles(raw[..., OFF_KC:OFF_KC + 1024])
+    vn = _nibbles(raw[..., OFF_VC:OFF_VC + 1024])
+    ck = np.zeros(lead + (PAGE, D), dtype=np.uint8)
+    cv = np.zeros(lead + (PAGE, D), dtype=np.uint8)
+    ck[..., K_TOK, K_CH] = kn
+    cv[..., V_TOK, V_CH] = vn
+    u16 = lambda a, b: np.ascontiguousarray(raw[..., a:b]).view(np.uint16)
+    return {
+        "ck": ck, "cv": cv,
+        "sk": u16(OFF_KS, OFF_KS + 256), "zk": u16(OFF_KZ, OFF_KZ + 256),
+        "sv": u16(OFF_VS, OFF_VS + 32), "zv": u16(OFF_VZ, OFF_VZ + 32),
+        "pad": raw[..., CHUNK_BYTES:CHUNK_STRIDE],
+    }
+
+
+def write_chunk(ck, sk, zk, cv, sv, zv):
+    """Logical page (one KV head) -> uint8 [CHUNK_STRIDE] (checker self-tests only)."""
+    raw = np.zeros(CHUNK_STRIDE, dtype=np.uint8)
+    kn = np.asarray(ck, dtype=np.uint8)[K_TOK, K_CH]
+    vn = np.asarray(cv, dtype=np.uint8)[V_TOK, V_CH]
+    raw[OFF_KC:OFF_KC + 1024] = kn[0::2] | (kn[1::2] << 4)
+    raw[OFF_VC:OFF_VC + 1024] = vn[0::2] | (vn[1::2] << 4)
+    raw[OFF_KS:OFF_KS + 256] = np.asarray(sk, dtype=np.float16).view(np.uint8)
+    raw[OFF_KZ:OFF_KZ + 256] = np.asarray(zk, dtype=np.float16).view(np.uint8)
+    raw[OFF_VS:OFF_VS + 32] = np.asarray(sv, dtype=np.float16).view(np.uint8)
+    raw[OFF_VZ:OFF_VZ + 32] = np.asarray(zv, dtype=np.float16).view(np.uint8)
+    return raw

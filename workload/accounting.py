@@ -1,0 +1,62 @@
+"""Byte accounting for the KV cache (host arithmetic for reports; no kernels).
+
+fp16 payload: the FP8 KV-cache capacity guide (adechristanto.de, section
+"Gewichte, laufenden Zustand und reservierten Speicher trennen") gives the
+unsharded KV payload as 2 x layers x KV heads x head_dim x held token
+positions x bytes per element, and notes that scale metadata and block
+rounding are not in it.
+
+int4 KIVI layout (this library's page format): per full 16-token page and KV
+head, K codes 16 x 128 nibbles (1024 B), V codes (1024 B), K scale and zero per
+channel (2 x 128 fp16 = 512 B), V scale and zero per token (2 x 16 fp16 = 64 B):
+2624 B, i.e. 164 B per token per KV head against 512 B in fp16. Tokens of the
+not yet full page are fp16 (512 B per token per KV head).
+"""
+
+import numpy as np
+
+PAGE = 16
+HEAD_DIM = 128
+CHUNK_BYTES = 2 * (PAGE * HEAD_DIM // 2) + 2 * 2 * HEAD_DIM + 2 * 2 * PAGE   # 2624
+FP16_TOKEN_BYTES = 2 * HEAD_DIM * 2                                           # K + V, 512
+
+
+def fp16_kv_bytes(layers, kv_heads, head_dim, tokens, bytes_per_elem=2):
+    """2 x layers x KV heads x head_dim x tokens x bytes (fp16 payload)."""
+    return 2 * layers * kv_heads * head_dim * tokens * bytes_per_elem
+
+
+def int4_bytes_per_token_per_head():
+    return CHUNK_BYTES / PAGE
+
+
+def density_vs_fp16():
+    return FP16_TOKEN_BYTES / int4_bytes_per_token_per_head()
+
+
+def cache_bytes(ctx_lens, kv_heads):
+    """Bytes of the int4 cache (full pages) plus the fp16 tail, one layer,
+    counting every sequence's pages (shared pages counted once per reader)."""
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    full = ctx // PAGE
+    tail = ctx % PAGE
+    return int(kv_heads * (full.sum() * CHUNK_BYTES + tail.sum() * FP16_TOKEN_BYTES))
+
+
+def decode_bytes(ctx_lens, num_q_heads, kv_heads):
+    """Algorithmic HBM bytes of one decode launch (one layer): the cache read
+    (pages and tails), the block-table entries of the full pages, the context
+    lengths, Q read and O written (fp16)."""
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    b = len(ctx)
+    full = ctx // PAGE
+    return int(cache_bytes(ctx, kv_heads) + 4 * full.sum() + 4 * b
+               + 2 * (2 * b * num_q_heads * HEAD_DIM))
+
+
+def quantize_bytes(n_tokens_flushed_pages, n_tail_tokens, kv_heads):
+    """Algorithmic bytes of a bulk prefill quantize: fp16 K/V read for every
+    token, int4 pages written for full pages, fp16 tail written."""
+    pages = n_tokens_flushed_pages // PAGE
+    return int(kv_heads * (n_tokens_flushed_pages * FP16_TOKEN_BYTES + pages * CHUNK_BYTES
+                           + 2 * n_tail_tokens * FP16_TOKEN_BYTES))
