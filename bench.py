@@ -1,0 +1,300 @@
+"""Benchmark of the int4 KIVI paged KV cache on one MI355X.
+
+A step is one decode step of the whole model-shaped stack: for every layer,
+s4kv_quantize_append of one new token per sequence (fp16 tail, page flush
+every 16th token) followed by s4kv_paged_decode over the int4 pages and the
+tail. Inputs (caches, queries, new tokens, context lengths) are resident in
+HBM before the timed region.
+
+Headline workload: Llama-3.1-8B-shaped decode, 32 layers, 32 query / 8 KV
+heads, head_dim 128, batch 128, contexts U[2048, 8192], page 16.
+Secondary (same JSON line): Llama-3-70B-shaped decode, 80 layers, 64/8 heads,
+batch 16, 32768-token contexts, with the bulk prefill quantize of those
+contexts timed separately.
+
+Prints one JSON line. `value` is KV GB/s: the algorithmic bytes of all decode
+launches of a step (pages, tails, block-table entries, Q, O) divided by the
+step time.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workload as W  # noqa: E402
+from workload import accounting as A  # noqa: E402
+
+METRIC = "int4 paged-decode KV GB/s + % of HBM peak; decode tokens/s at 8B/70B shapes"
+HBM_PEAK_GBS = 8000.0
+
+
+def _sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "int4_kivi_quantized_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Model:
+    """All layers of one workload: per-layer caches over one shared block table."""
+
+    def __init__(self, wl, extra_steps, time_prefill=False):
+        import torch
+        from int4_kivi_quantized_amd import Shape
+        from int4_kivi_quantized_amd.cache import LayerCache
+
+        self.wl = wl
+        self.ctx0 = W.context_lengths(wl)
+        self.plan = W.plan_pages(wl, self.ctx0, extra_steps)
+        self.shape = Shape(wl.batch, wl.hq, wl.hkv, self.plan.num_pages, self.plan.max_pages)
+        self.bt = torch.from_numpy(self.plan.block_table).cuda()
+        self.layers = []
+        self.q = []
+        self.mults = []
+        self.prefill_ms = 0.0
+        self.prefill_bytes = 0
+        counts = self.ctx0.astype(np.int64)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device="cuda")
+        sl = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+        for layer in range(wl.layers):
+            cache = LayerCache(self.shape)
+            mult = W.k_channel_multipliers(wl, layer)
+            ks, vs = [], []
+            for b in range(wl.batch):
+                k, v = W.sequence_kv(wl, layer, b, int(self.ctx0[b]), "cuda", mult)
+                ks.append(k)
+                vs.append(v)
+            k_all = torch.cat(ks).contiguous()
+            v_all = torch.cat(vs).contiguous()
+            del ks, vs
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            cache.append(k_all, v_all, cu, sl, int(counts.max()), self.bt)
+            e1.record()
+            torch.cuda.synchronize()
+            if time_prefill:
+                self.prefill_ms += e0.elapsed_time(e1)
+                full = (counts // 16) * 16
+                self.prefill_bytes += A.quantize_bytes(int(full.sum()), int((counts - full).sum()), wl.hkv)
+            del k_all, v_all
+            self.layers.append(cache)
+            self.q.append(W.queries(wl, layer, "cuda"))
+            self.mults.append(mult)
+        torch.cuda.synchronize()
+
+
+def run_decode_bench(wl, steps, warmup, append):
+    import torch
+
+    total = steps + warmup
+    model = Model(wl, total if append else 0, time_prefill=not append)
+    B = wl.batch
+    max_ctx = int(model.ctx0.max()) + (total if append else 0)
+    cu1 = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    slots, ctxs, new = [], [], []
+    for s in range(total):
+        add = s if append else 0
+        slots.append(torch.tensor((model.ctx0 + add).astype(np.int32), device="cuda"))
+        ctxs.append(torch.tensor((model.ctx0 + add + (1 if append else 0)).astype(np.int32), device="cuda"))
+    if append:
+        for layer in range(wl.layers):
+            # one pre-drawn new token per sequence and layer, appended every step
+            k, v = W.new_tokens(wl, layer, 0, "cuda", model.mults[layer])
+            new.append((k.contiguous(), v.contiguous()))
+    outs = [torch.empty_like(q) for q in model.q]
+    for c in model.layers:
+        c.workspace(max_ctx)
+    torch.cuda.synchronize()
+
+    n_ev = steps * wl.layers
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(s, timed_idx=None):
+        for layer, cache in enumerate(model.layers):
+            if append:
+                cache.append(new[layer][0], new[layer][1], cu1, slots[s], 1, model.bt)
+            if timed_idx is not None:
+                ev_a[timed_idx * wl.layers + layer].record()
+            cache.decode(model.q[layer], model.bt, ctxs[s], max_ctx, out=outs[layer])
+            if timed_idx is not None:
+                ev_b[timed_idx * wl.layers + layer].record()
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(warmup + i, i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+
+    # algorithmic bytes of the decode launches, per layer, averaged over timed steps
+    per_layer = [A.decode_bytes(model.ctx0 + (warmup + i + (1 if append else 0) if append else 0),
+                                wl.hq, wl.hkv) for i in range(steps)]
+    dec_bytes = float(np.mean(per_layer))
+    step_bytes = dec_bytes * wl.layers
+    res = {
+        "step_ms": step_ms,
+        "wall_s": wall,
+        "kv_gbs": step_bytes / (step_ms * 1e-3) / 1e9,
+        "tokens_per_s": B / (step_ms * 1e-3),
+        "decode_launch_ms": dec_ms,
+        "decode_launch_bytes": dec_bytes,
+        "decode_launch_gbs": dec_bytes / (dec_ms * 1e-3) / 1e9,
+        "model": model,
+    }
+    if not append:
+        res["prefill_gbs"] = model.prefill_bytes / (model.prefill_ms * 1e-3) / 1e9 if model.prefill_ms else None
+        res["prefill_ms_per_layer"] = model.prefill_ms / wl.layers
+    return res
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The CPU oracle on a bounded sample of the same workload: decode
+    attention (dequantize + softmax attention) of layer 0 for as many
+    sequences as fit in about `budget_s` seconds; quantization of the sample
+    happens before the clock starts."""
+    import oracle
+    import threadpoolctl
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    ctx = W.context_lengths(wl)
+    mult = W.k_channel_multipliers(wl, 0)
+    q = W.queries(wl, 0, "cpu").numpy()
+    done, nbytes, elapsed = 0, 0, 0.0
+    for b in range(wl.batch):
+        k, v = W.sequence_kv(wl, 0, b, int(ctx[b]), "cpu", mult)
+        c = oracle.sequence_cache(k.numpy(), v.numpy())
+        t = time.perf_counter()
+        kh, vh = oracle.dequantized_sequence(c)
+        oracle.decode_attention(q[b], kh, vh)
+        elapsed += time.perf_counter() - t
+        done += 1
+        nbytes += A.decode_bytes(ctx[b:b + 1], wl.hq, wl.hkv)
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": nbytes / elapsed / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{wl.name} layer 0, {done} of {wl.batch} sequences, one decode each "
+                  f"({elapsed:.1f} s of CPU time)",
+        "tokens_per_s_one_layer": done / elapsed,
+    }
+
+
+def load_traffic(digest):
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("sources_digest") != digest:
+        return None
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3.1-8b-decode", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the int4 KIVI decode "
+              "path here is a single-GPU kernel library with no collectives", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int4_kivi_quantized_amd import s4kv
+    s4kv.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    wl = W.WORKLOADS[args.workload]
+    print(f"[bench] {wl.name}: layers={wl.layers} B={wl.batch} Hq={wl.hq} Hkv={wl.hkv} "
+          f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    r = run_decode_bench(wl, args.steps, args.warmup, append=wl.append)
+    del r["model"]
+    torch.cuda.empty_cache()
+    print(f"[bench] step {r['step_ms']:.3f} ms, {r['kv_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    digest = _sources_digest(["paged_decode.hip", "internal.h"])
+    traffic = load_traffic(digest)
+    line = {
+        "metric": METRIC,
+        "value": round(r["kv_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 cache (u4 codes, f16 scale/zero), f16 q/o, f32 softmax",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "layers": wl.layers, "batch": wl.batch, "q_heads": wl.hq,
+            "kv_heads": wl.hkv, "head_dim": wl.head_dim, "page": wl.page,
+            "ctx": list(wl.ctx), "append_per_step": 1 if wl.append else 0,
+        },
+        "hbm_peak_frac": round(r["kv_gbs"] / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(r["tokens_per_s"], 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "s4kv_paged_decode call (split decode + split reduce), one layer",
+            "achieved": round(r["decode_launch_gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["decode_launch_gbs"] / HBM_PEAK_GBS, 4),
+            "avg_launch_ms": round(r["decode_launch_ms"], 5),
+            "bytes_per_launch": int(r["decode_launch_bytes"]),
+            "traffic": (traffic or {}).get("hbm_bytes_per_launch"),
+        },
+    }
+    if not args.no_secondary and wl.name != "llama3-70b":
+        wl2 = W.WORKLOADS["llama3-70b"]
+        print(f"[bench] secondary {wl2.name}", file=sys.stderr, flush=True)
+        r2 = run_decode_bench(wl2, max(3, args.steps // 4), 1, append=False)
+        del r2["model"]
+        torch.cuda.empty_cache()
+        line["secondary"] = {
+            "workload": wl2.name, "layers": wl2.layers, "batch": wl2.batch,
+            "ms_per_step": round(r2["step_ms"], 4), "kv_gbs": round(r2["kv_gbs"], 2),
+            "hbm_peak_frac": round(r2["kv_gbs"] / HBM_PEAK_GBS, 4),
+            "decode_tokens_per_s": round(r2["tokens_per_s"], 1),
+            "decode_launch_gbs": round(r2["decode_launch_gbs"], 2),
+            "prefill_quantize_gbs": None if r2["prefill_gbs"] is None else round(r2["prefill_gbs"], 2),
+            "prefill_ms_per_layer": round(r2["prefill_ms_per_layer"], 4),
+        }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
