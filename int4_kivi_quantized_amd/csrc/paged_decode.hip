@@ -1,15 +1,36 @@
-// Split-K paged decode over the int4 KIVI cache (gfx950), vector-ALU version.
+// Split-K paged decode over the int4 KIVI cache on gfx950 matrix cores.
 //
-// Method: S4 KV product page ("Funktionsweise" step 1): paged-attention KV
-// cache stored as int4, KEY per channel, VALUE per token; the decode step is
-// standard attention (header paragraph: head_dim 128, standard attention).
+// Method: S4 KV product page ("Funktionsweise" step 1): the paged-attention KV
+// cache is stored as int4, KEY per channel (scale/zero per channel for each
+// 16-token page), VALUE per token (scale/zero per token); the decode step is
+// standard attention (header paragraph: head_dim 128, standard attention),
+// with the G = Hq/Hkv query heads of a KV head reading the same pages (GQA,
+// KV-cache explainer, "Begriffe", entry "Grouped-Query Attention").
 //
-// One 64-lane work-group per (split, KV head, sequence). A split is a run of
-// consecutive logical pages of one sequence; the last split of a sequence
-// also takes the fp16 tail. Each work-group keeps an online softmax (running
-// max m, running sum l, unnormalized output o) for the G query heads that
-// share its KV head and writes (m, l, o) to the workspace; the reduce kernel
-// merges the splits of a sequence into O.
+// Work decomposition: one 64-lane wave per (split, KV head, sequence). A split
+// is a run of consecutive logical pages of one sequence (an even number, so
+// pages are taken in pairs); the last split of a sequence also takes the fp16
+// tail. The wave keeps an online softmax (running max in log2 units, running
+// sum, unnormalized output) for its G query heads and writes it to the
+// workspace; splitk_reduce_kernel merges the splits of each sequence.
+//
+// Dense contractions on v_mfma_f32_16x16x32_f16 (D = A x B, 16x32 by 32x16):
+//  * logits, transposed: S^T[token][col] = sum_d codeK[token][d] * qs[d][col]
+//    with qs = q * sK (the per-channel K scale folded into the query, per page)
+//    plus the zero-point term sum_d q[d] * zK[d] (one number per head and page).
+//    For G <= 8 the 16 columns hold the G heads for page A and for page B of a
+//    pair, so one B operand serves two pages.
+//  * output, transposed: O^T[d][col] += sum_slot codeV^T[d][slot] * ps[slot][col]
+//    with ps = p * sV (the per-token V scale folded into the probabilities); the
+//    32 K-slots are 4 tokens of page A and 4 of page B per lane group. For
+//    G <= 8, columns [0,G) carry the fp16 high part of ps and [G,2G) the low
+//    part; for G > 8 the two parts go through two products.
+//  * fp16 hi/lo pairs keep ~22 significant bits in qs and ps, so the products
+//    add no error beyond fp32 accumulation order.
+//  * the 4-bit codes enter the matrix cores as fp16 subnormals: masking a
+//    packed dword with 0x000F000F gives two codes as c * 2^-24, with 0x00F000F0
+//    two more as c * 2^-20. Those scale factors are folded into the other
+//    operand, so unpacking costs one shift and four ANDs per eight codes.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -20,147 +41,394 @@
 namespace s4kv {
 namespace {
 
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
 constexpr float kNegInf = -INFINITY;
+constexpr float kLog2e = 1.4426950408889634f;
+// Codes are fed as c * 2^-24 (slots 0,1,4,5) and c * 2^-20 (slots 2,3,6,7);
+// the query side carries 2^-4 and 2^-8 on those slots so every product is
+// c * q * s * 2^-28, and the output side carries 1 and 1/16 so every product
+// is c * p * s * 2^-24.
+constexpr float kQkUnscale = 268435456.0f;  // 2^28
+constexpr float kPvUnscale = 16777216.0f;   // 2^24
 
-__device__ inline float nib(const uint8_t* base, int byte, int k) {
-  return static_cast<float>((base[byte] >> (4 * (k & 1))) & 0xF);
+__device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
+
+__device__ inline f4 mfma(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// K code of (token t, channel d) inside a staged chunk (s4kv.h page format).
-__device__ inline float k_code(const uint8_t* c, int t, int d) {
-  const int m = d >> 5, g = (d & 31) >> 3, e = d & 7;
-  const int kk = 4 * (e & 1) + (e >> 1);
-  return nib(c + kOffKCodes, 16 * (16 * g + t) + 4 * m + (kk >> 1), kk);
+// Eight K codes of one dword -> the 8 A-operand elements of one logits product.
+__device__ inline h8 k_operand(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  u4 v;
+  v[0] = w & 0x000F000Fu;
+  v[1] = w & 0x00F000F0u;
+  v[2] = w8 & 0x000F000Fu;
+  v[3] = w8 & 0x00F000F0u;
+  return as_h8(v);
 }
 
-// V code of (token t, channel d).
-__device__ inline float v_code(const uint8_t* c, int t, int d) {
-  const int tau = d >> 4, r = d & 15, g = t >> 2, j = t & 3;
-  const int m = tau >> 1;
-  const int kk = 4 * (j & 1) + 2 * (tau & 1) + (j >> 1);
-  return nib(c + kOffVCodes, 16 * (16 * g + r) + 4 * m + (kk >> 1), kk);
+// V operand of tile pair (2m, 2m+1) from dword m of page A (wa) and page B (wb).
+__device__ inline void v_operands(uint32_t wa, uint32_t wb, h8& even, h8& odd) {
+  const uint32_t a8 = wa >> 8, b8 = wb >> 8;
+  u4 e, o;
+  e[0] = wa & 0x000F000Fu; e[1] = wa & 0x00F000F0u; e[2] = wb & 0x000F000Fu; e[3] = wb & 0x00F000F0u;
+  o[0] = a8 & 0x000F000Fu; o[1] = a8 & 0x00F000F0u; o[2] = b8 & 0x000F000Fu; o[3] = b8 & 0x00F000F0u;
+  even = as_h8(e);
+  odd = as_h8(o);
+}
+
+__device__ inline u4 ld16(const uint8_t* p) { return *reinterpret_cast<const u4*>(p); }
+__device__ inline u2 ld8(const uint8_t* p) { return *reinterpret_cast<const u2*>(p); }
+
+__device__ inline _Float16 h_at(u4 v, int i) { return __builtin_bit_cast(h8, v)[i]; }
+__device__ inline _Float16 h_at2(u2 v, int i) {
+  return __builtin_bit_cast(h2v, (uint32_t)v[i >> 1])[i & 1];
+}
+
+// qs = qc * s as an fp16 (hi, lo) pair for the 8 elements of one product.
+__device__ inline void qs_split(h8 qc, u4 s, h8& hi, h8& lo) {
+  const h8 sv = as_h8(s);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = static_cast<float>(qc[i]) * static_cast<float>(sv[i]);
+    const _Float16 xh = static_cast<_Float16>(x);
+    hi[i] = xh;
+    lo[i] = static_cast<_Float16>(x - static_cast<float>(xh));
+  }
+}
+
+// sum_d q[d] * z[d] over this lane's 32 channels; qc carries 2^-4 on slots
+// 0,1,4,5 and 2^-8 on slots 2,3,6,7.
+__device__ inline float zero_term(const h8 (&qc)[4], const u4 (&z)[4]) {
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const h8 zz = as_h8(z[m]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = static_cast<float>(qc[m][i]) * static_cast<float>(zz[i]);
+      if ((i & 2) == 0) a += t; else b += t;
+    }
+  }
+  return 16.f * a + 256.f * b;
+}
+
+struct PageLoads {
+  u4 kc;     // K codes, this lane's 16-byte block
+  u4 vc;     // V codes
+  u2 sv, zv; // V scale/zero of tokens 4g..4g+3
+};
+
+__device__ inline PageLoads load_page(const uint8_t* chunk, int lane, int g) {
+  PageLoads r;
+  r.kc = ld16(chunk + kOffKCodes + 16 * lane);
+  r.vc = ld16(chunk + kOffVCodes + 16 * lane);
+  r.sv = ld8(chunk + kOffVScale + 8 * g);
+  r.zv = ld8(chunk + kOffVZero + 8 * g);
+  return r;
+}
+
+__device__ inline void load_kmeta(const uint8_t* chunk, int g, u4 (&s)[4], u4 (&z)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    s[m] = ld16(chunk + kOffKScale + 64 * m + 16 * g);
+    z[m] = ld16(chunk + kOffKZero + 64 * m + 16 * g);
+  }
 }
 
 template <int G>
-__global__ __launch_bounds__(64) void decode_valu_kernel(
+__global__ __launch_bounds__(64) void decode_mfma_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ pages,
     const __half* __restrict__ tail_k, const __half* __restrict__ tail_v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int32_t max_pages,
     int32_t hkv, int32_t pps, int32_t max_splits, float sm_scale, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
+  constexpr bool kPacked = (G <= 8);  // two pages share the logits B operand
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
+  const int c = lane & 15, g = lane >> 4;
   const int hq = hkv * G;
+
   // ctx is clamped to what the block table and the launch can address, so a
   // broken precondition gives a wrong answer, never an out-of-bounds access.
   const int ctx = min(ctx_lens[b], max_pages * kPage);
   const int full = ctx > 0 ? ctx / kPage : 0;
-  const int tail = ctx > 0 ? ctx % kPage : 0;
+  const int tail_n = ctx > 0 ? ctx % kPage : 0;
   const int nsplit = min(max_splits, max(1, (full + pps - 1) / pps));
   if (split >= nsplit) return;
   const int pbeg = split * pps;
   const int pend = (split == nsplit - 1) ? full : min(full, pbeg + pps);
-  const bool do_tail = (split == nsplit - 1) && tail > 0;
+  const bool do_tail = (split == nsplit - 1) && tail_n > 0;
 
-  __shared__ float qs[G][kHeadDim];
-  __shared__ __align__(16) uint8_t chunk[kChunkBytes];
-  __shared__ float lg[G][kPage];
+  // Column roles. Packed: [0,G) = (head c, page A), [G,2G) = (head c-G, page B);
+  // later columns mirror column c % G of page A so they stay finite.
+  int head, pslot;
+  head = c % G;
+  pslot = (kPacked && c >= G && c < 2 * G) ? 1 : 0;
+  const bool lo_col = kPacked ? (c >= G && c < 2 * G) : false;
+  const int partner = kPacked ? (16 * g + ((c < G) ? c + G : (c < 2 * G ? c - G : c))) : lane;
+  const int my_head = h * G + head;  // query head of this lane's column
 
-  for (int i = lane; i < G * kHeadDim; i += 64)
-    qs[i / kHeadDim][i % kHeadDim] = __half2float(q[((int64_t)b * hq + h * G) * kHeadDim + i]);
-
-  float m_run[G], l_run[G], o0[G], o1[G];
+  // Query in the logits B layout: element i of product m is channel 32m+8g+i,
+  // pre-scaled by 2^-4 (slots 0,1,4,5) or 2^-8 (slots 2,3,6,7).
+  h8 qc[4];
+  {
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + my_head) * kHeadDim);
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) { m_run[hh] = kNegInf; l_run[hh] = 0.f; o0[hh] = 0.f; o1[hh] = 0.f; }
-
-  const int qt = lane & 15, qu = lane >> 4;  // QK mapping: token, channel quarter
-  const int d0 = 2 * lane;                   // PV mapping: channel pair
-
-  const int npg = (pend - pbeg) + (do_tail ? 1 : 0);
-  for (int it = 0; it < npg; ++it) {
-    const bool is_tail = (pbeg + it >= pend);
-    const int ntok = is_tail ? tail : kPage;
-    const __half* tk = tail_k + ((int64_t)b * hkv + h) * kPage * kHeadDim;
-    const __half* tv = tail_v + ((int64_t)b * hkv + h) * kPage * kHeadDim;
-    __syncthreads();
-    if (!is_tail) {
-      const uint8_t* src = pages + ((int64_t)block_table[(int64_t)b * max_pages + pbeg + it] * hkv + h) * kChunkStride;
-      for (int i = lane; i < kChunkBytes / 16; i += 64)
-        reinterpret_cast<uint4*>(chunk)[i] = reinterpret_cast<const uint4*>(src)[i];
+    for (int m = 0; m < 4; ++m) {
+      const h8 v = as_h8(ld16(qrow + 2 * (32 * m + 8 * g)));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        qc[m][i] = static_cast<_Float16>(static_cast<float>(v[i]) * (((i & 2) == 0) ? 0.0625f : 0.00390625f));
     }
-    __syncthreads();
-    // ---- logits: lane (token qt, channels 32*qu .. +32) ----
-    float acc[G];
+  }
+
+  const float l2s = sm_scale * kLog2e;  // logits go to log2 units
+  float m_run = kNegInf, l_part = 0.f, lz_part = 0.f;
+  f4 o[8];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
-    if (qt < ntok) {
-      for (int i = 0; i < 32; ++i) {
-        const int d = 32 * qu + i;
-        float kh;
-        if (is_tail) {
-          kh = __half2float(tk[qt * kHeadDim + d]);
-        } else {
-          const float s = __half2float(reinterpret_cast<const __half*>(chunk + kOffKScale)[d]);
-          const float z = __half2float(reinterpret_cast<const __half*>(chunk + kOffKZero)[d]);
-          kh = k_code(chunk, qt, d) * s + z;
-        }
+  for (int t = 0; t < 8; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // Online-softmax update for one block: lg[0..3] page A tokens 4g+i of this
+  // lane's head, lg[4..7] page B (after the exchange), in log2 units. Returns
+  // p in the same order, rescaling the state when the running max grows.
+  auto softmax_block = [&](float (&lg)[8], float (&p)[8]) {
+    float mb = lg[0];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) acc[hh] += qs[hh][d] * kh;
+    for (int i = 1; i < 8; ++i) mb = fmaxf(mb, lg[i]);
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mnew = fmaxf(m_run, mb);
+    if (__any(mnew > m_run)) {
+      const float alpha = (mnew == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      l_part *= alpha;
+      lz_part *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+      m_run = mnew;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - m_run);
+  };
+
+  // ps = p * sV * (1 or 1/16 by slot) as the PV B operands (hi, lo).
+  auto ps_operands = [&](const float (&p)[8], u2 svA, u2 svB, h8& bhi, h8& blo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sv = static_cast<float>(i < 4 ? h_at2(svA, i) : h_at2(svB, i - 4));
+      const float x = p[i] * sv * (((i & 2) == 0) ? 1.0f : 0.0625f);
+      const _Float16 xh = static_cast<_Float16>(x);
+      bhi[i] = xh;
+      blo[i] = static_cast<_Float16>(x - static_cast<float>(xh));
+    }
+  };
+
+  // ------------------------------------------------------------ fp16 tail
+  if (do_tail) {
+    __shared__ _Float16 tv_s[kPage][kHeadDim];
+    const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)b * hkv + h) * kPage * kHeadDim);
+    const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)b * hkv + h) * kPage * kHeadDim);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<u4*>(&tv_s[0][0])[lane + 64 * i] = ld16(tv + 16 * (lane + 64 * i));
+    // logits: A = K tail values (token c, channels 32m+8g..+8), B = plain q
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + my_head) * kHeadDim);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const h8 ka = as_h8(ld16(tk + 2 * (c * kHeadDim + 32 * m + 8 * g)));
+      const h8 qb = as_h8(ld16(qrow + 2 * (32 * m + 8 * g)));
+      acc = mfma(ka, qb, acc);
+    }
+    float lg[8], p[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = (pslot == 0) && (4 * g + i < tail_n);
+      lg[i] = valid ? acc[i] * l2s : kNegInf;
+    }
+    if (kPacked) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[4 + i] = __shfl(lg[i], partner);
+      if (pslot == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { const float t = lg[i]; lg[i] = lg[4 + i]; lg[4 + i] = t; }
       }
-    }
+    } else {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      acc[hh] += __shfl_xor(acc[hh], 16);
-      acc[hh] += __shfl_xor(acc[hh], 32);
+      for (int i = 0; i < 4; ++i) lg[4 + i] = kNegInf;
     }
-    if (qu == 0) {
+    softmax_block(lg, p);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) lg[hh][qt] = (qt < ntok) ? acc[hh] * sm_scale : kNegInf;
-    }
+    for (int i = 0; i < 4; ++i) l_part += p[i];
     __syncthreads();
-    // ---- online softmax + PV: lane owns channels d0, d0+1 ----
+    // output: A = V tail values of tokens 4g..4g+3 (slots 0..3), slots 4..7 empty
+    h8 bhi, blo;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float pm = kNegInf;
-      for (int t = 0; t < ntok; ++t) pm = fmaxf(pm, lg[hh][t]);
-      const float mnew = fmaxf(m_run[hh], pm);
-      const float alpha = (m_run[hh] == kNegInf) ? 0.f : expf(m_run[hh] - mnew);
-      m_run[hh] = mnew;
-      l_run[hh] *= alpha;
-      o0[hh] *= alpha;
-      o1[hh] *= alpha;
+    for (int i = 0; i < 8; ++i) {
+      const float x = (i < 4) ? p[i] : 0.f;
+      const _Float16 xh = static_cast<_Float16>(x);
+      bhi[i] = xh;
+      blo[i] = static_cast<_Float16>(x - static_cast<float>(xh));
     }
-    for (int t = 0; t < ntok; ++t) {
-      float v0, v1;
-      if (is_tail) {
-        v0 = __half2float(tv[t * kHeadDim + d0]);
-        v1 = __half2float(tv[t * kHeadDim + d0 + 1]);
+    const h8 bsel = lo_col ? blo : bhi;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      h8 a;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = (4 * g + i < tail_n) ? tv_s[4 * g + i][16 * t + c] : static_cast<_Float16>(0.f);
+        a[4 + i] = static_cast<_Float16>(0.f);
+      }
+      if (kPacked) {
+        o[t] = mfma(a, bsel, o[t]);
       } else {
-        const float s = __half2float(reinterpret_cast<const __half*>(chunk + kOffVScale)[t]);
-        const float z = __half2float(reinterpret_cast<const __half*>(chunk + kOffVZero)[t]);
-        v0 = v_code(chunk, t, d0) * s + z;
-        v1 = v_code(chunk, t, d0 + 1) * s + z;
+        o[t] = mfma(a, bhi, o[t]);
+        o[t] = mfma(a, blo, o[t]);
       }
+    }
+    // bring the tail's contribution to the page accumulators' scale (exact)
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float p = expf(lg[hh][t] - m_run[hh]);
-        l_run[hh] += p;
-        o0[hh] += p * v0;
-        o1[hh] += p * v1;
+    for (int t = 0; t < 8; ++t) o[t] *= (1.0f / kPvUnscale);
+  }
+
+  // ------------------------------------------------------------ int4 pages
+  const int32_t* bt = block_table + (int64_t)b * max_pages;
+  const int64_t head_off = (int64_t)h * kChunkStride;
+  const int64_t page_stride = (int64_t)hkv * kChunkStride;
+  const float qk_scale = l2s * kQkUnscale;
+
+  for (int pa = pbeg; pa < pend; pa += 2) {
+    const bool has_b = (pa + 1 < pend);
+    const uint8_t* chA = pages + bt[pa] * page_stride + head_off;
+    const uint8_t* chB = has_b ? pages + bt[pa + 1] * page_stride + head_off : chA;
+    const PageLoads LA = load_page(chA, lane, g);
+    const PageLoads LB = load_page(chB, lane, g);
+
+    // ---- logits ----
+    f4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+    float ztA, ztB;
+    if (kPacked) {
+      u4 s[4], z[4];
+      load_kmeta(pslot ? chB : chA, g, s, z);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        h8 hi, lo;
+        qs_split(qc[m], s[m], hi, lo);
+        const h8 ka = k_operand(LA.kc[m]);
+        const h8 kb = k_operand(LB.kc[m]);
+        accA = mfma(ka, hi, accA);
+        accA = mfma(ka, lo, accA);
+        accB = mfma(kb, hi, accB);
+        accB = mfma(kb, lo, accB);
+      }
+      float zt = zero_term(qc, z);
+      zt += __shfl_xor(zt, 16);
+      zt += __shfl_xor(zt, 32);
+      ztA = zt;
+      ztB = zt;
+    } else {
+      u4 sa[4], za[4], sb[4], zb[4];
+      load_kmeta(chA, g, sa, za);
+      load_kmeta(chB, g, sb, zb);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        h8 hi, lo;
+        qs_split(qc[m], sa[m], hi, lo);
+        const h8 ka = k_operand(LA.kc[m]);
+        accA = mfma(ka, hi, accA);
+        accA = mfma(ka, lo, accA);
+        qs_split(qc[m], sb[m], hi, lo);
+        const h8 kb = k_operand(LB.kc[m]);
+        accB = mfma(kb, hi, accB);
+        accB = mfma(kb, lo, accB);
+      }
+      ztA = zero_term(qc, za);
+      ztA += __shfl_xor(ztA, 16);
+      ztA += __shfl_xor(ztA, 32);
+      ztB = zero_term(qc, zb);
+      ztB += __shfl_xor(ztB, 16);
+      ztB += __shfl_xor(ztB, 32);
+    }
+
+    float lg[8], p[8];
+    if (kPacked) {
+      // this lane's own page: A for pslot 0, B for pslot 1
+      const f4 mine = pslot ? accB : accA;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[i] = (pslot && !has_b) ? kNegInf : (mine[i] * qk_scale + ztA * l2s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[4 + i] = __shfl(lg[i], partner);
+      if (pslot == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { const float t = lg[i]; lg[i] = lg[4 + i]; lg[4 + i] = t; }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lg[i] = accA[i] * qk_scale + ztA * l2s;
+        lg[4 + i] = has_b ? (accB[i] * qk_scale + ztB * l2s) : kNegInf;
+      }
+    }
+    softmax_block(lg, p);
+
+    // ---- running sums and the output product ----
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l_part += p[i] + p[4 + i];
+      lz_part += p[i] * static_cast<float>(h_at2(LA.zv, i)) + p[4 + i] * static_cast<float>(h_at2(LB.zv, i));
+    }
+    h8 bhi, blo;
+    ps_operands(p, LA.sv, LB.sv, bhi, blo);
+    const h8 bsel = lo_col ? blo : bhi;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      h8 ve, vo;
+      v_operands(LA.vc[m], LB.vc[m], ve, vo);
+      if (kPacked) {
+        o[2 * m] = mfma(ve, bsel, o[2 * m]);
+        o[2 * m + 1] = mfma(vo, bsel, o[2 * m + 1]);
+      } else {
+        o[2 * m] = mfma(ve, bhi, o[2 * m]);
+        o[2 * m] = mfma(ve, blo, o[2 * m]);
+        o[2 * m + 1] = mfma(vo, bhi, o[2 * m + 1]);
+        o[2 * m + 1] = mfma(vo, blo, o[2 * m + 1]);
       }
     }
   }
 
+  // ------------------------------------------------------------ write partials
+  l_part += __shfl_xor(l_part, 16);
+  l_part += __shfl_xor(l_part, 32);
+  lz_part += __shfl_xor(lz_part, 16);
+  lz_part += __shfl_xor(lz_part, 32);
+  if (kPacked) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const int64_t row = ((int64_t)b * hq + h * G + hh) * max_splits + split;
-    reinterpret_cast<float2*>(ws_o + row * kHeadDim)[lane] = make_float2(o0[hh], o1[hh]);
-    if (lane == 0) { ws_ml[2 * row] = m_run[hh]; ws_ml[2 * row + 1] = l_run[hh]; }
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[t][i] += __shfl(o[t][i], partner);
+  }
+  if (c < G) {
+    const int64_t row = ((int64_t)b * hq + h * G + c) * max_splits + split;
+    float* dst = ws_o + row * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = o[t][i] * kPvUnscale + lz_part;
+      *reinterpret_cast<f4*>(dst + 16 * t + 4 * g) = v;
+    }
+    if (g == 0) { ws_ml[2 * row] = m_run; ws_ml[2 * row + 1] = l_part; }
   }
 }
 
-// Merge the splits of (sequence, query head): M = max m_s,
-// O = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+// Merge the splits of (sequence, query head), m in log2 units:
+// M = max m_s, O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 __global__ __launch_bounds__(128) void splitk_reduce_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ ctx_lens, int32_t max_pages, int32_t hq, int32_t pps,
@@ -177,7 +445,7 @@ __global__ __launch_bounds__(128) void splitk_reduce_kernel(
   float den = 0.f, num = 0.f;
   for (int s = 0; s < nsplit; ++s) {
     const float ms = ws_ml[2 * (row0 + s)];
-    const float w = (ms == kNegInf) ? 0.f : expf(ms - mx);
+    const float w = (ms == kNegInf) ? 0.f : exp2f(ms - mx);
     den += w * ws_ml[2 * (row0 + s) + 1];
     num += w * ws_o[(row0 + s) * kHeadDim + d];
   }
@@ -190,7 +458,7 @@ hipError_t launch_g(const s4kv_shape& s, const SplitPlan& plan, const void* q, c
                     const int32_t* ctx_lens, float sm_scale, float* ws_o, float* ws_ml,
                     hipStream_t stream) {
   dim3 grid(plan.max_splits, s.num_kv_heads, s.num_seqs);
-  hipLaunchKernelGGL((decode_valu_kernel<G>), grid, dim3(64), 0, stream,
+  hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(64), 0, stream,
                      static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
                      static_cast<const __half*>(tail_k), static_cast<const __half*>(tail_v),
                      block_table, ctx_lens, s.max_pages_per_seq, s.num_kv_heads,
@@ -203,7 +471,8 @@ hipError_t launch_g(const s4kv_shape& s, const SplitPlan& plan, const void* q, c
 SplitPlan plan_splits(const s4kv_shape& s, int32_t max_ctx) {
   const int64_t max_full = max_ctx / kPage;
   // Aim for about 8192 work-groups over the whole batch when every sequence
-  // is at max_ctx; never fewer than 8 pages per work-group.
+  // is at max_ctx; never fewer than 8 pages per work-group; an even count so
+  // pages pair up inside a split.
   const int64_t work = (int64_t)s.num_seqs * s.num_kv_heads * max_full;
   int64_t pps = (work + 8191) / 8192;
   if (pps < 8) pps = 8;
@@ -244,8 +513,7 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const SplitPlan& plan, const
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_q_heads, s.num_seqs), dim3(kHeadDim), 0,
                      stream, ws_o, ws_ml, ctx_lens, s.max_pages_per_seq, s.num_q_heads,
-                     plan.pages_per_split,
-                     plan.max_splits, static_cast<__half*>(out));
+                     plan.pages_per_split, plan.max_splits, static_cast<__half*>(out));
   return hipGetLastError();
 }
 
