@@ -55,6 +55,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // is c * p * s * 2^-24.
 constexpr float kQkUnscale = 268435456.0f;  // 2^28
 constexpr float kPvUnscale = 16777216.0f;   // 2^24
+constexpr int kMaxSplitPages = 64;          // one block id per lane of a wave
 
 __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 
@@ -92,64 +93,69 @@ __device__ inline _Float16 h_at2(u2 v, int i) {
 }
 
 // qs = qc * s as an fp16 (hi, lo) pair for the 8 elements of one product.
+// qc * s is exact in fp32 (two 11-bit significands), so hi = fp16(qc*s) and
+// lo = fp16(qc*s - hi) are each rounded once.
 __device__ inline void qs_split(h8 qc, u4 s, h8& hi, h8& lo) {
   const h8 sv = as_h8(s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float x = static_cast<float>(qc[i]) * static_cast<float>(sv[i]);
-    const _Float16 xh = static_cast<_Float16>(x);
+    const float a = static_cast<float>(qc[i]), b = static_cast<float>(sv[i]);
+    const _Float16 xh = static_cast<_Float16>(__builtin_fmaf(a, b, 0.0f));
     hi[i] = xh;
-    lo[i] = static_cast<_Float16>(x - static_cast<float>(xh));
+    lo[i] = static_cast<_Float16>(__builtin_fmaf(a, b, -static_cast<float>(xh)));
   }
 }
 
-// sum_d q[d] * z[d] over this lane's 32 channels; qc carries 2^-4 on slots
-// 0,1,4,5 and 2^-8 on slots 2,3,6,7.
+__device__ inline h2v half_pair(h8 v, int k) { return h2v{v[2 * k], v[2 * k + 1]}; }
+
+// sum_d q[d] * z[d] over this lane's 32 channels (dot2 on fp16 pairs); qc
+// carries 2^-4 on slots 0,1,4,5 and 2^-8 on slots 2,3,6,7.
 __device__ inline float zero_term(const h8 (&qc)[4], const u4 (&z)[4]) {
   float a = 0.f, b = 0.f;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const h8 zz = as_h8(z[m]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float t = static_cast<float>(qc[m][i]) * static_cast<float>(zz[i]);
-      if ((i & 2) == 0) a += t; else b += t;
-    }
+    a = __builtin_amdgcn_fdot2(half_pair(qc[m], 0), half_pair(zz, 0), a, false);
+    b = __builtin_amdgcn_fdot2(half_pair(qc[m], 1), half_pair(zz, 1), b, false);
+    a = __builtin_amdgcn_fdot2(half_pair(qc[m], 2), half_pair(zz, 2), a, false);
+    b = __builtin_amdgcn_fdot2(half_pair(qc[m], 3), half_pair(zz, 3), b, false);
   }
   return 16.f * a + 256.f * b;
 }
 
-struct PageLoads {
-  u4 kc;     // K codes, this lane's 16-byte block
-  u4 vc;     // V codes
-  u2 sv, zv; // V scale/zero of tokens 4g..4g+3
+// Everything one lane loads for a pair of pages. The K scale/zero block of
+// both pages (2 x 512 B) comes in as one coalesced 16-byte load per lane and
+// is spread through LDS, since every lane needs 32 scales and 32 zeros.
+struct PairData {
+  u4 kcA, kcB;  // K codes, this lane's 16-byte block of page A / page B
+  u4 vcA, vcB;  // V codes
+  u2 svA, svB;  // V scales of tokens 4g..4g+3
+  u2 zvA, zvB;  // V zeros of tokens 4g..4g+3
+  u4 kmeta;     // lanes 0-31: 16 B of page A's K scale/zero block; 32-63: page B's
 };
 
-__device__ inline PageLoads load_page(const uint8_t* chunk, int lane, int g) {
-  PageLoads r;
-  r.kc = ld16(chunk + kOffKCodes + 16 * lane);
-  r.vc = ld16(chunk + kOffVCodes + 16 * lane);
-  r.sv = ld8(chunk + kOffVScale + 8 * g);
-  r.zv = ld8(chunk + kOffVZero + 8 * g);
-  return r;
-}
-
-__device__ inline void load_kmeta(const uint8_t* chunk, int g, u4 (&s)[4], u4 (&z)[4]) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    s[m] = ld16(chunk + kOffKScale + 64 * m + 16 * g);
-    z[m] = ld16(chunk + kOffKZero + 64 * m + 16 * g);
-  }
+__device__ inline void load_pair(const uint8_t* chA, const uint8_t* chB, int lane, int g,
+                                 PairData& d) {
+  d.kcA = ld16(chA + kOffKCodes + 16 * lane);
+  d.kcB = ld16(chB + kOffKCodes + 16 * lane);
+  d.vcA = ld16(chA + kOffVCodes + 16 * lane);
+  d.vcB = ld16(chB + kOffVCodes + 16 * lane);
+  d.svA = ld8(chA + kOffVScale + 8 * g);
+  d.svB = ld8(chB + kOffVScale + 8 * g);
+  d.zvA = ld8(chA + kOffVZero + 8 * g);
+  d.zvB = ld8(chB + kOffVZero + 8 * g);
+  d.kmeta = ld16((lane < 32 ? chA : chB) + kOffKScale + 16 * (lane & 31));
 }
 
 template <int G>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ pages,
     const __half* __restrict__ tail_k, const __half* __restrict__ tail_v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int32_t max_pages,
     int32_t hkv, int32_t pps, int32_t max_splits, float sm_scale, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
   constexpr bool kPacked = (G <= 8);  // two pages share the logits B operand
+  constexpr bool kPow2 = (G & (G - 1)) == 0;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
@@ -163,16 +169,21 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const int nsplit = min(max_splits, max(1, (full + pps - 1) / pps));
   if (split >= nsplit) return;
   const int pbeg = split * pps;
-  const int pend = (split == nsplit - 1) ? full : min(full, pbeg + pps);
+  const int pend = (split == nsplit - 1) ? min(full, pbeg + kMaxSplitPages) : min(full, pbeg + pps);
+  const int npg = max(0, pend - pbeg);
   const bool do_tail = (split == nsplit - 1) && tail_n > 0;
 
   // Column roles. Packed: [0,G) = (head c, page A), [G,2G) = (head c-G, page B);
   // later columns mirror column c % G of page A so they stay finite.
-  int head, pslot;
-  head = c % G;
-  pslot = (kPacked && c >= G && c < 2 * G) ? 1 : 0;
-  const bool lo_col = kPacked ? (c >= G && c < 2 * G) : false;
+  const int head = c % G;
+  const int pslot = (kPacked && c >= G && c < 2 * G) ? 1 : 0;
+  const bool lo_col = kPacked && c >= G && c < 2 * G;
+  // the lane holding the same head for the other page of the pair
   const int partner = kPacked ? (16 * g + ((c < G) ? c + G : (c < 2 * G ? c - G : c))) : lane;
+  auto xchg = [&](float v) -> float {
+    if constexpr (kPacked && kPow2) return __shfl_xor(v, G);
+    else return __shfl(v, partner);
+  };
   const int my_head = h * G + head;  // query head of this lane's column
 
   // Query in the logits B layout: element i of product m is channel 32m+8g+i,
@@ -195,15 +206,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < 8; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // Online-softmax update for one block: lg[0..3] page A tokens 4g+i of this
-  // lane's head, lg[4..7] page B (after the exchange), in log2 units. Returns
-  // p in the same order, rescaling the state when the running max grows.
-  auto softmax_block = [&](float (&lg)[8], float (&p)[8]) {
-    float mb = lg[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mb = fmaxf(mb, lg[i]);
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+  auto rescale_to = [&](float mb) {
     const float mnew = fmaxf(m_run, mb);
     if (__any(mnew > m_run)) {
       const float alpha = (mnew == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
@@ -212,20 +215,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 #pragma unroll
       for (int t = 0; t < 8; ++t) o[t] *= alpha;
       m_run = mnew;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - m_run);
-  };
-
-  // ps = p * sV * (1 or 1/16 by slot) as the PV B operands (hi, lo).
-  auto ps_operands = [&](const float (&p)[8], u2 svA, u2 svB, h8& bhi, h8& blo) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float sv = static_cast<float>(i < 4 ? h_at2(svA, i) : h_at2(svB, i - 4));
-      const float x = p[i] * sv * (((i & 2) == 0) ? 1.0f : 0.0625f);
-      const _Float16 xh = static_cast<_Float16>(x);
-      bhi[i] = xh;
-      blo[i] = static_cast<_Float16>(x - static_cast<float>(xh));
     }
   };
 
@@ -246,26 +235,25 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       const h8 qb = as_h8(ld16(qrow + 2 * (32 * m + 8 * g)));
       acc = mfma(ka, qb, acc);
     }
-    float lg[8], p[8];
+    // every lane holds the tail logits of its head (all columns saw the tail)
+    float lg[4];
+    float mb = kNegInf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool valid = (pslot == 0) && (4 * g + i < tail_n);
-      lg[i] = valid ? acc[i] * l2s : kNegInf;
+      lg[i] = (4 * g + i < tail_n) ? acc[i] * l2s : kNegInf;
+      mb = fmaxf(mb, lg[i]);
     }
-    if (kPacked) {
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    rescale_to(mb);
+    float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lg[4 + i] = __shfl(lg[i], partner);
-      if (pslot == 1) {
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - m_run);
+    // the tail counts once per head: on page-A lanes only
+    if (pslot == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { const float t = lg[i]; lg[i] = lg[4 + i]; lg[4 + i] = t; }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lg[4 + i] = kNegInf;
+      for (int i = 0; i < 4; ++i) l_part += p[i];
     }
-    softmax_block(lg, p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) l_part += p[i];
     __syncthreads();
     // output: A = V tail values of tokens 4g..4g+3 (slots 0..3), slots 4..7 empty
     h8 bhi, blo;
@@ -285,7 +273,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         a[i] = (4 * g + i < tail_n) ? tv_s[4 * g + i][16 * t + c] : static_cast<_Float16>(0.f);
         a[4 + i] = static_cast<_Float16>(0.f);
       }
-      if (kPacked) {
+      if constexpr (kPacked) {
         o[t] = mfma(a, bsel, o[t]);
       } else {
         o[t] = mfma(a, bhi, o[t]);
@@ -298,99 +286,140 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   }
 
   // ------------------------------------------------------------ int4 pages
-  const int32_t* bt = block_table + (int64_t)b * max_pages;
+  // block ids of this split, one per lane (a split has at most 64 pages)
+  const int bt_lane = (lane < npg) ? block_table[(int64_t)b * max_pages + pbeg + lane] : 0;
   const int64_t head_off = (int64_t)h * kChunkStride;
   const int64_t page_stride = (int64_t)hkv * kChunkStride;
   const float qk_scale = l2s * kQkUnscale;
+  const int npairs = (npg + 1) >> 1;
 
-  for (int pa = pbeg; pa < pend; pa += 2) {
-    const bool has_b = (pa + 1 < pend);
-    const uint8_t* chA = pages + bt[pa] * page_stride + head_off;
-    const uint8_t* chB = has_b ? pages + bt[pa + 1] * page_stride + head_off : chA;
-    const PageLoads LA = load_page(chA, lane, g);
-    const PageLoads LB = load_page(chB, lane, g);
+  auto chunk_at = [&](int idx) -> const uint8_t* {
+    const int bid = __builtin_amdgcn_readlane(bt_lane, idx);
+    return pages + (int64_t)bid * page_stride + head_off;
+  };
+  auto fetch = [&](int i, PairData& d) {
+    const int ia = 2 * i;
+    const int ib = min(2 * i + 1, npg - 1);
+    load_pair(chunk_at(ia), chunk_at(ib), lane, g, d);
+  };
 
+  // K scale/zero blocks of the pair being processed: [page][32 x 16 B]
+  __shared__ u4 kmeta_s[2][32];
+  auto kmeta_read = [&](int page, u4 (&sc)[4], u4 (&ze)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      sc[m] = kmeta_s[page][4 * m + g];        // scale, channels 32m+8g..+8
+      ze[m] = kmeta_s[page][16 + 4 * m + g];   // zero, same channels
+    }
+  };
+
+  auto process = [&](const PairData& d, int i) {
+    const bool has_b = (2 * i + 1 < npg);
+    __builtin_amdgcn_wave_barrier();
+    kmeta_s[lane >> 5][lane & 31] = d.kmeta;
+    __builtin_amdgcn_wave_barrier();
     // ---- logits ----
     f4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
-    float ztA, ztB;
-    if (kPacked) {
-      u4 s[4], z[4];
-      load_kmeta(pslot ? chB : chA, g, s, z);
+    float lgA[4], lgB[4];
+    float p_own[4], pA[4], pB[4];
+    if constexpr (kPacked) {
+      u4 sc[4], ze[4];
+      kmeta_read(pslot, sc, ze);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
-        qs_split(qc[m], s[m], hi, lo);
-        const h8 ka = k_operand(LA.kc[m]);
-        const h8 kb = k_operand(LB.kc[m]);
+        qs_split(qc[m], sc[m], hi, lo);
+        const h8 ka = k_operand(d.kcA[m]);
+        const h8 kb = k_operand(d.kcB[m]);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      float zt = zero_term(qc, z);
+      float zt = zero_term(qc, ze);
       zt += __shfl_xor(zt, 16);
       zt += __shfl_xor(zt, 32);
-      ztA = zt;
-      ztB = zt;
+      const float zl = zt * l2s;
+      const f4 mine = pslot ? accB : accA;
+      const bool valid = !(pslot && !has_b);
+      float mb = kNegInf;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lgA[k] = valid ? mine[k] * qk_scale + zl : kNegInf;
+        mb = fmaxf(mb, lgA[k]);
+      }
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      mb = fmaxf(mb, xchg(mb));
+      rescale_to(mb);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p_own[k] = __builtin_amdgcn_exp2f(lgA[k] - m_run);
+      const u2 zv = pslot ? d.zvB : d.zvA;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        l_part += p_own[k];
+        lz_part += p_own[k] * static_cast<float>(h_at2(zv, k));
+        const float other = xchg(p_own[k]);
+        pA[k] = pslot ? other : p_own[k];
+        pB[k] = pslot ? p_own[k] : other;
+      }
     } else {
-      u4 sa[4], za[4], sb[4], zb[4];
-      load_kmeta(chA, g, sa, za);
-      load_kmeta(chB, g, sb, zb);
+      u4 scA[4], zeA[4], scB[4], zeB[4];
+      kmeta_read(0, scA, zeA);
+      kmeta_read(1, scB, zeB);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
-        qs_split(qc[m], sa[m], hi, lo);
-        const h8 ka = k_operand(LA.kc[m]);
+        qs_split(qc[m], scA[m], hi, lo);
+        const h8 ka = k_operand(d.kcA[m]);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
-        qs_split(qc[m], sb[m], hi, lo);
-        const h8 kb = k_operand(LB.kc[m]);
+        qs_split(qc[m], scB[m], hi, lo);
+        const h8 kb = k_operand(d.kcB[m]);
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      ztA = zero_term(qc, za);
-      ztA += __shfl_xor(ztA, 16);
-      ztA += __shfl_xor(ztA, 32);
-      ztB = zero_term(qc, zb);
-      ztB += __shfl_xor(ztB, 16);
-      ztB += __shfl_xor(ztB, 32);
-    }
-
-    float lg[8], p[8];
-    if (kPacked) {
-      // this lane's own page: A for pslot 0, B for pslot 1
-      const f4 mine = pslot ? accB : accA;
+      float zA = zero_term(qc, zeA);
+      zA += __shfl_xor(zA, 16);
+      zA += __shfl_xor(zA, 32);
+      float zB = zero_term(qc, zeB);
+      zB += __shfl_xor(zB, 16);
+      zB += __shfl_xor(zB, 32);
+      float mb = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lg[i] = (pslot && !has_b) ? kNegInf : (mine[i] * qk_scale + ztA * l2s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lg[4 + i] = __shfl(lg[i], partner);
-      if (pslot == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { const float t = lg[i]; lg[i] = lg[4 + i]; lg[4 + i] = t; }
+      for (int k = 0; k < 4; ++k) {
+        lgA[k] = accA[k] * qk_scale + zA * l2s;
+        lgB[k] = has_b ? accB[k] * qk_scale + zB * l2s : kNegInf;
+        mb = fmaxf(mb, fmaxf(lgA[k], lgB[k]));
       }
-    } else {
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      rescale_to(mb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lg[i] = accA[i] * qk_scale + ztA * l2s;
-        lg[4 + i] = has_b ? (accB[i] * qk_scale + ztB * l2s) : kNegInf;
+      for (int k = 0; k < 4; ++k) {
+        pA[k] = __builtin_amdgcn_exp2f(lgA[k] - m_run);
+        pB[k] = __builtin_amdgcn_exp2f(lgB[k] - m_run);
+        l_part += pA[k] + pB[k];
+        lz_part += pA[k] * static_cast<float>(h_at2(d.zvA, k)) + pB[k] * static_cast<float>(h_at2(d.zvB, k));
       }
     }
-    softmax_block(lg, p);
-
-    // ---- running sums and the output product ----
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      l_part += p[i] + p[4 + i];
-      lz_part += p[i] * static_cast<float>(h_at2(LA.zv, i)) + p[4 + i] * static_cast<float>(h_at2(LB.zv, i));
-    }
+    // ---- output product: ps = p * sV (1 or 1/16 by slot), fp16 hi/lo ----
     h8 bhi, blo;
-    ps_operands(p, LA.sv, LB.sv, bhi, blo);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float pk = (k < 4) ? pA[k] : pB[k - 4];
+      const float sv = static_cast<float>(k < 4 ? h_at2(d.svA, k) : h_at2(d.svB, k - 4)) *
+                       (((k & 2) == 0) ? 1.0f : 0.0625f);
+      const _Float16 xh = static_cast<_Float16>(__builtin_fmaf(pk, sv, 0.0f));
+      bhi[k] = xh;
+      blo[k] = static_cast<_Float16>(__builtin_fmaf(pk, sv, -static_cast<float>(xh)));
+    }
     const h8 bsel = lo_col ? blo : bhi;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       h8 ve, vo;
-      v_operands(LA.vc[m], LB.vc[m], ve, vo);
-      if (kPacked) {
+      v_operands(d.vcA[m], d.vcB[m], ve, vo);
+      if constexpr (kPacked) {
         o[2 * m] = mfma(ve, bsel, o[2 * m]);
         o[2 * m + 1] = mfma(vo, bsel, o[2 * m + 1]);
       } else {
@@ -400,18 +429,36 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         o[2 * m + 1] = mfma(vo, blo, o[2 * m + 1]);
       }
     }
+  };
+
+  // two register buffers: the next pair is in flight while one is processed
+  if (npairs > 0) {
+    PairData d0, d1;
+    fetch(0, d0);
+    for (int i = 0; i < npairs; i += 2) {
+      if (i + 1 < npairs) fetch(i + 1, d1);
+      process(d0, i);
+      if (i + 1 >= npairs) break;
+      if (i + 2 < npairs) fetch(i + 2, d0);
+      process(d1, i + 1);
+    }
   }
 
   // ------------------------------------------------------------ write partials
+  if constexpr (kPacked) {
+    // page-A and page-B lanes of a head each summed their own tokens
+    l_part += xchg(l_part);
+    lz_part += xchg(lz_part);
+  }
   l_part += __shfl_xor(l_part, 16);
   l_part += __shfl_xor(l_part, 32);
   lz_part += __shfl_xor(lz_part, 16);
   lz_part += __shfl_xor(lz_part, 32);
-  if (kPacked) {
+  if constexpr (kPacked) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[t][i] += __shfl(o[t][i], partner);
+      for (int i = 0; i < 4; ++i) o[t][i] += xchg(o[t][i]);
   }
   if (c < G) {
     const int64_t row = ((int64_t)b * hq + h * G + c) * max_splits + split;
@@ -471,11 +518,12 @@ hipError_t launch_g(const s4kv_shape& s, const SplitPlan& plan, const void* q, c
 SplitPlan plan_splits(const s4kv_shape& s, int32_t max_ctx) {
   const int64_t max_full = max_ctx / kPage;
   // Aim for about 8192 work-groups over the whole batch when every sequence
-  // is at max_ctx; never fewer than 8 pages per work-group; an even count so
-  // pages pair up inside a split.
+  // is at max_ctx; 8 to 64 pages per work-group (the block ids of a split sit
+  // one per lane); an even count so pages pair up inside a split.
   const int64_t work = (int64_t)s.num_seqs * s.num_kv_heads * max_full;
   int64_t pps = (work + 8191) / 8192;
   if (pps < 8) pps = 8;
+  if (pps > kMaxSplitPages) pps = kMaxSplitPages;
   pps = (pps + 1) & ~int64_t(1);
   SplitPlan p;
   p.pages_per_split = static_cast<int>(pps);
