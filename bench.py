@@ -222,6 +222,9 @@ def main():
     ap.add_argument("--workload", default="llama3.1-8b-decode", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="profiling only: override the workload's layer count (the JSON "
+                         "line then does not describe the named workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the int4 KIVI decode "
@@ -234,6 +237,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     wl = W.WORKLOADS[args.workload]
+    if args.layers is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, layers=args.layers)
+        args.no_secondary = True
     print(f"[bench] {wl.name}: layers={wl.layers} B={wl.batch} Hq={wl.hq} Hkv={wl.hkv} "
           f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     r = run_decode_bench(wl, args.steps, args.warmup, append=wl.append)
@@ -260,6 +267,7 @@ def main():
             "workload": wl.name, "layers": wl.layers, "batch": wl.batch, "q_heads": wl.hq,
             "kv_heads": wl.hkv, "head_dim": wl.head_dim, "page": wl.page,
             "ctx": list(wl.ctx), "append_per_step": 1 if wl.append else 0,
+            "profiling_layer_override": args.layers,
         },
         "hbm_peak_frac": round(r["kv_gbs"] / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(r["tokens_per_s"], 1),

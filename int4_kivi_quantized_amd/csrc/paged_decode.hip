@@ -123,29 +123,33 @@ __device__ inline float zero_term(const h8 (&qc)[4], const u4 (&z)[4]) {
   return 16.f * a + 256.f * b;
 }
 
-// Everything one lane loads for a pair of pages. The K scale/zero block of
-// both pages (2 x 512 B) comes in as one coalesced 16-byte load per lane and
-// is spread through LDS, since every lane needs 32 scales and 32 zeros.
-struct PairData {
-  u4 kcA, kcB;  // K codes, this lane's 16-byte block of page A / page B
-  u4 vcA, vcB;  // V codes
-  u2 svA, svB;  // V scales of tokens 4g..4g+3
-  u2 zvA, zvB;  // V zeros of tokens 4g..4g+3
-  u4 kmeta;     // lanes 0-31: 16 B of page A's K scale/zero block; 32-63: page B's
-};
+// A stage holds one pair of pages, copied HBM -> LDS by the DMA path
+// (global_load_lds_dwordx4: lane l writes 16 bytes at stage base + 16 l):
+//   [   0,1024) K codes page A     [1024,2048) K codes page B
+//   [2048,3072) V codes page A     [3072,4096) V codes page B
+//   [4096,4608) K scale+zero A     [4608,5120) K scale+zero B
+//   [5120,5184) V scale+zero A     [5184,5248) V scale+zero B
+constexpr int kStageBytes = 5248;
+constexpr int kStages = 3;          // two pairs in flight while one is consumed
+constexpr int kDmaPerStage = 6;     // DMA instructions issued per stage
 
-__device__ inline void load_pair(const uint8_t* chA, const uint8_t* chB, int lane, int g,
-                                 PairData& d) {
-  d.kcA = ld16(chA + kOffKCodes + 16 * lane);
-  d.kcB = ld16(chB + kOffKCodes + 16 * lane);
-  d.vcA = ld16(chA + kOffVCodes + 16 * lane);
-  d.vcB = ld16(chB + kOffVCodes + 16 * lane);
-  d.svA = ld8(chA + kOffVScale + 8 * g);
-  d.svB = ld8(chB + kOffVScale + 8 * g);
-  d.zvA = ld8(chA + kOffVZero + 8 * g);
-  d.zvB = ld8(chB + kOffVZero + 8 * g);
-  d.kmeta = ld16((lane < 32 ? chA : chB) + kOffKScale + 16 * (lane & 31));
+__device__ inline void dma16(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
 }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// wait for all LDS / scalar-memory operations of this wave
+__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+// the compiler does not know the DMA writes LDS: keep memory accesses on
+// their side of the waits
+__device__ inline void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
 
 template <int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(
@@ -218,9 +222,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
   };
 
+  // ------------------------------------------------------------ int4 pages
+  // block ids of this split, one per lane (a split has at most 64 pages)
+  const int bt_lane = (lane < npg) ? block_table[(int64_t)b * max_pages + pbeg + lane] : 0;
+  const int64_t head_off = (int64_t)h * kChunkStride;
+  const int64_t page_stride = (int64_t)hkv * kChunkStride;
+  const float qk_scale = l2s * kQkUnscale;
+  const int npairs = (npg + 1) >> 1;
+
+  auto chunk_at = [&](int idx) -> const uint8_t* {
+    const int bid = __builtin_amdgcn_readlane(bt_lane, idx);
+    return pages + (int64_t)bid * page_stride + head_off;
+  };
+  __shared__ __align__(16) uint8_t stage_s[kStages][kStageBytes];
+
+  // Issue the DMA of pair i into its stage (block ids come from the lanes).
+  auto issue = [&](int i) {
+    const uint8_t* chA = chunk_at(2 * i);
+    const uint8_t* chB = chunk_at(min(2 * i + 1, npg - 1));
+    uint8_t* st = stage_s[i % kStages];
+    dma16(chA + kOffKCodes + 16 * lane, st + 0);
+    dma16(chB + kOffKCodes + 16 * lane, st + 1024);
+    dma16(chA + kOffVCodes + 16 * lane, st + 2048);
+    dma16(chB + kOffVCodes + 16 * lane, st + 3072);
+    dma16((lane < 32 ? chA : chB) + kOffKScale + 16 * (lane & 31), st + 4096);
+    if (lane < 8) dma16((lane < 4 ? chA : chB) + kOffVScale + 16 * (lane & 3), st + 5120);
+  };
+
+  if (npairs > 0) issue(0);
+  if (npairs > 1) issue(1);
+
   // ------------------------------------------------------------ fp16 tail
+  // (processed while the first two page pairs are in flight)
   if (do_tail) {
-    __shared__ _Float16 tv_s[kPage][kHeadDim];
+    // the third stage is not written before the loop starts: stage the tail V there
+    _Float16 (*tv_s)[kHeadDim] = reinterpret_cast<_Float16 (*)[kHeadDim]>(&stage_s[kStages - 1][0]);
     const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)b * hkv + h) * kPage * kHeadDim);
     const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)b * hkv + h) * kPage * kHeadDim);
 #pragma unroll
@@ -285,39 +321,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int t = 0; t < 8; ++t) o[t] *= (1.0f / kPvUnscale);
   }
 
-  // ------------------------------------------------------------ int4 pages
-  // block ids of this split, one per lane (a split has at most 64 pages)
-  const int bt_lane = (lane < npg) ? block_table[(int64_t)b * max_pages + pbeg + lane] : 0;
-  const int64_t head_off = (int64_t)h * kChunkStride;
-  const int64_t page_stride = (int64_t)hkv * kChunkStride;
-  const float qk_scale = l2s * kQkUnscale;
-  const int npairs = (npg + 1) >> 1;
 
-  auto chunk_at = [&](int idx) -> const uint8_t* {
-    const int bid = __builtin_amdgcn_readlane(bt_lane, idx);
-    return pages + (int64_t)bid * page_stride + head_off;
-  };
-  auto fetch = [&](int i, PairData& d) {
-    const int ia = 2 * i;
-    const int ib = min(2 * i + 1, npg - 1);
-    load_pair(chunk_at(ia), chunk_at(ib), lane, g, d);
-  };
-
-  // K scale/zero blocks of the pair being processed: [page][32 x 16 B]
-  __shared__ u4 kmeta_s[2][32];
-  auto kmeta_read = [&](int page, u4 (&sc)[4], u4 (&ze)[4]) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      sc[m] = kmeta_s[page][4 * m + g];        // scale, channels 32m+8g..+8
-      ze[m] = kmeta_s[page][16 + 4 * m + g];   // zero, same channels
-    }
-  };
-
-  auto process = [&](const PairData& d, int i) {
+  auto process = [&](int i) {
     const bool has_b = (2 * i + 1 < npg);
-    __builtin_amdgcn_wave_barrier();
-    kmeta_s[lane >> 5][lane & 31] = d.kmeta;
-    __builtin_amdgcn_wave_barrier();
+    const uint8_t* st = stage_s[i % kStages];
+    const u4 kcA = *reinterpret_cast<const u4*>(st + 16 * lane);
+    const u4 kcB = *reinterpret_cast<const u4*>(st + 1024 + 16 * lane);
+    const u4 vcA = *reinterpret_cast<const u4*>(st + 2048 + 16 * lane);
+    const u4 vcB = *reinterpret_cast<const u4*>(st + 3072 + 16 * lane);
+    const u2 svA = *reinterpret_cast<const u2*>(st + 5120 + 8 * g);
+    const u2 zvA = *reinterpret_cast<const u2*>(st + 5120 + 32 + 8 * g);
+    const u2 svB = *reinterpret_cast<const u2*>(st + 5184 + 8 * g);
+    const u2 zvB = *reinterpret_cast<const u2*>(st + 5184 + 32 + 8 * g);
+    auto kmeta_read = [&](int page, u4 (&sc)[4], u4 (&ze)[4]) {
+      const uint8_t* km = st + 4096 + 512 * page;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        sc[m] = *reinterpret_cast<const u4*>(km + 64 * m + 16 * g);        // scale, ch 32m+8g..
+        ze[m] = *reinterpret_cast<const u4*>(km + 256 + 64 * m + 16 * g);  // zero, same channels
+      }
+    };
     // ---- logits ----
     f4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
     float lgA[4], lgB[4];
@@ -329,8 +352,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
         qs_split(qc[m], sc[m], hi, lo);
-        const h8 ka = k_operand(d.kcA[m]);
-        const h8 kb = k_operand(d.kcB[m]);
+        const h8 ka = k_operand(kcA[m]);
+        const h8 kb = k_operand(kcB[m]);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
         accB = mfma(kb, hi, accB);
@@ -354,7 +377,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       rescale_to(mb);
 #pragma unroll
       for (int k = 0; k < 4; ++k) p_own[k] = __builtin_amdgcn_exp2f(lgA[k] - m_run);
-      const u2 zv = pslot ? d.zvB : d.zvA;
+      const u2 zv = pslot ? zvB : zvA;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         l_part += p_own[k];
@@ -371,11 +394,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
         qs_split(qc[m], scA[m], hi, lo);
-        const h8 ka = k_operand(d.kcA[m]);
+        const h8 ka = k_operand(kcA[m]);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
         qs_split(qc[m], scB[m], hi, lo);
-        const h8 kb = k_operand(d.kcB[m]);
+        const h8 kb = k_operand(kcB[m]);
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
@@ -400,7 +423,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         pA[k] = __builtin_amdgcn_exp2f(lgA[k] - m_run);
         pB[k] = __builtin_amdgcn_exp2f(lgB[k] - m_run);
         l_part += pA[k] + pB[k];
-        lz_part += pA[k] * static_cast<float>(h_at2(d.zvA, k)) + pB[k] * static_cast<float>(h_at2(d.zvB, k));
+        lz_part += pA[k] * static_cast<float>(h_at2(zvA, k)) + pB[k] * static_cast<float>(h_at2(zvB, k));
       }
     }
     // ---- output product: ps = p * sV (1 or 1/16 by slot), fp16 hi/lo ----
@@ -408,7 +431,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float pk = (k < 4) ? pA[k] : pB[k - 4];
-      const float sv = static_cast<float>(k < 4 ? h_at2(d.svA, k) : h_at2(d.svB, k - 4)) *
+      const float sv = static_cast<float>(k < 4 ? h_at2(svA, k) : h_at2(svB, k - 4)) *
                        (((k & 2) == 0) ? 1.0f : 0.0625f);
       const _Float16 xh = static_cast<_Float16>(__builtin_fmaf(pk, sv, 0.0f));
       bhi[k] = xh;
@@ -418,7 +441,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       h8 ve, vo;
-      v_operands(d.vcA[m], d.vcB[m], ve, vo);
+      v_operands(vcA[m], vcB[m], ve, vo);
       if constexpr (kPacked) {
         o[2 * m] = mfma(ve, bsel, o[2 * m]);
         o[2 * m + 1] = mfma(vo, bsel, o[2 * m + 1]);
@@ -431,17 +454,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
   };
 
-  // two register buffers: the next pair is in flight while one is processed
-  if (npairs > 0) {
-    PairData d0, d1;
-    fetch(0, d0);
-    for (int i = 0; i < npairs; i += 2) {
-      if (i + 1 < npairs) fetch(i + 1, d1);
-      process(d0, i);
-      if (i + 1 >= npairs) break;
-      if (i + 2 < npairs) fetch(i + 2, d0);
-      process(d1, i + 1);
+  // Pipeline: pairs i+1 and i+2 are in flight (HBM -> LDS) while pair i is
+  // consumed. vmcnt counts this wave's outstanding vector-memory operations
+  // in issue order, so "at most 6 * (pairs issued after i)" means pair i has
+  // landed; nothing else in this loop touches vector memory.
+  for (int i = 0; i < npairs; ++i) {
+    wait_lgkmcnt0();   // the stage about to be refilled has been read out
+    compiler_fence();
+    if (i + 2 < npairs) {
+      issue(i + 2);
+      wait_vmcnt<2 * kDmaPerStage>();
+    } else if (i + 1 < npairs) {
+      wait_vmcnt<kDmaPerStage>();
+    } else {
+      wait_vmcnt<0>();
     }
+    compiler_fence();
+    process(i);
+    compiler_fence();
   }
 
   // ------------------------------------------------------------ write partials
