@@ -20,8 +20,10 @@ s4kv_status check_shape(const s4kv_shape* s) {
   // launch-grid limits (y and z dimensions)
   if (s->num_kv_heads > 65535 || s->num_seqs > 65535 || s->num_q_heads > 65535)
     return S4KV_ERR_UNSUPPORTED;
-  // block-table products must fit in int32 page counts
+  // token positions and the flat unit count (B * Hkv * (pages + 1)) must fit in int32
   if ((int64_t)s->max_pages_per_seq * S4KV_PAGE_SIZE > INT32_MAX) return S4KV_ERR_INVALID_ARG;
+  if ((int64_t)s->num_seqs * s->num_kv_heads * ((int64_t)s->max_pages_per_seq + 1) > INT32_MAX)
+    return S4KV_ERR_INVALID_ARG;
   return S4KV_OK;
 }
 
@@ -72,7 +74,7 @@ s4kv_status s4kv_quantize_append(const s4kv_shape* shape, const void* k, const v
 
 size_t s4kv_decode_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx) {
   if (check_shape(shape) != S4KV_OK || max_ctx < 1) return 0;
-  return s4kv::workspace_bytes(*shape, s4kv::plan_splits(*shape, max_ctx));
+  return s4kv::workspace_bytes(*shape);
 }
 
 s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void* pages,
@@ -86,9 +88,8 @@ s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void
     return S4KV_ERR_INVALID_ARG;
   if (!q || !pages || !tail_k || !tail_v || !block_table || !ctx_lens || !out || !workspace)
     return S4KV_ERR_INVALID_ARG;
-  const s4kv::SplitPlan plan = s4kv::plan_splits(*shape, max_ctx);
-  if (workspace_bytes < s4kv::workspace_bytes(*shape, plan)) return S4KV_ERR_WORKSPACE;
-  const hipError_t e = s4kv::launch_paged_decode(*shape, plan, q, pages, tail_k, tail_v,
+  if (workspace_bytes < s4kv::workspace_bytes(*shape)) return S4KV_ERR_WORKSPACE;
+  const hipError_t e = s4kv::launch_paged_decode(*shape, q, pages, tail_k, tail_v,
                                                  block_table, ctx_lens, sm_scale, out, workspace,
                                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;

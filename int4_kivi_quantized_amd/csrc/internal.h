@@ -22,20 +22,15 @@ constexpr int kOffKZero = 2304;
 constexpr int kOffVScale = 2560;
 constexpr int kOffVZero = 2592;
 
-// Decode split plan: pages handled by one work-group, number of splits.
-struct SplitPlan {
-  int pages_per_split;
-  int max_splits;
-};
-SplitPlan plan_splits(const s4kv_shape& s, int32_t max_ctx);
-size_t workspace_bytes(const s4kv_shape& s, const SplitPlan& plan);
+// Decode workspace: unit prefix sums and the per-(sequence, head, wave) partials.
+size_t workspace_bytes(const s4kv_shape& s);
 
 hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void* v,
                                   const int32_t* cu_new, const int32_t* slot, int32_t max_new,
                                   const int32_t* block_table, void* pages, void* tail_k,
                                   void* tail_v, hipStream_t stream);
 
-hipError_t launch_paged_decode(const s4kv_shape& s, const SplitPlan& plan, const void* q,
+hipError_t launch_paged_decode(const s4kv_shape& s, const void* q,
                                const void* pages, const void* tail_k, const void* tail_v,
                                const int32_t* block_table, const int32_t* ctx_lens,
                                float sm_scale, void* out, void* workspace, hipStream_t stream);

@@ -7,12 +7,18 @@
 // with the G = Hq/Hkv query heads of a KV head reading the same pages (GQA,
 // KV-cache explainer, "Begriffe", entry "Grouped-Query Attention").
 //
-// Work decomposition: one 64-lane wave per (split, KV head, sequence). A split
-// is a run of consecutive logical pages of one sequence (an even number, so
-// pages are taken in pairs); the last split of a sequence also takes the fp16
-// tail. The wave keeps an online softmax (running max in log2 units, running
-// sum, unnormalized output) for its G query heads and writes it to the
-// workspace; splitk_reduce_kernel merges the splits of each sequence.
+// Work decomposition (persistent, balanced): the work of one launch is the flat
+// list of "units" over (sequence b, KV head h) in order, a unit being one full
+// int4 page or the fp16 tail of (b, h). decode_plan_kernel writes the prefix
+// sums of units per sequence; then a fixed grid of W one-wave work-groups (as
+// many as the GPU keeps resident) splits the list into W equal contiguous
+// ranges. Each wave streams its range through a 3-stage HBM -> LDS DMA ring,
+// pairing consecutive pages of the same (b, h), and keeps an online softmax
+// (running max in log2 units, running sum, unnormalized output) for the G
+// query heads of the current (b, h); when its range crosses into the next
+// (b, h) it writes the partial result to workspace slot (b*Hkv + h) + wave.
+// splitk_reduce_kernel merges, for each (b, query head), the partials of the
+// consecutive waves whose ranges touched it.
 //
 // Dense contractions on v_mfma_f32_16x16x32_f16 (D = A x B, 16x32 by 32x16):
 //  * logits, transposed: S^T[token][col] = sum_d codeK[token][d] * qs[d][col]
@@ -55,7 +61,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // is c * p * s * 2^-24.
 constexpr float kQkUnscale = 268435456.0f;  // 2^28
 constexpr float kPvUnscale = 16777216.0f;   // 2^24
-constexpr int kMaxSplitPages = 64;          // one block id per lane of a wave
+constexpr int kMaxWaves = 4096;             // upper bound on the persistent grid
 
 __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 
@@ -92,18 +98,14 @@ __device__ inline _Float16 h_at2(u2 v, int i) {
   return __builtin_bit_cast(h2v, (uint32_t)v[i >> 1])[i & 1];
 }
 
-// qs = qc * s as an fp16 (hi, lo) pair for the 8 elements of one product.
-// qc * s is exact in fp32 (two 11-bit significands), so hi = fp16(qc*s) and
-// lo = fp16(qc*s - hi) are each rounded once.
+// qs = qc * s as an fp16 (hi, lo) pair for the 8 elements of one product,
+// two elements per packed fp16 instruction: hi = fp16(qc*s) (one rounding of
+// the exact product) and lo = fma(qc, s, -hi) (exact product minus hi, one
+// rounding), so hi + lo carries about 22 significant bits of qc*s.
 __device__ inline void qs_split(h8 qc, u4 s, h8& hi, h8& lo) {
   const h8 sv = as_h8(s);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = static_cast<float>(qc[i]), b = static_cast<float>(sv[i]);
-    const _Float16 xh = static_cast<_Float16>(__builtin_fmaf(a, b, 0.0f));
-    hi[i] = xh;
-    lo[i] = static_cast<_Float16>(__builtin_fmaf(a, b, -static_cast<float>(xh)));
-  }
+  hi = qc * sv;
+  lo = __builtin_elementwise_fma(qc, sv, -hi);
 }
 
 __device__ inline h2v half_pair(h8 v, int k) { return h2v{v[2 * k], v[2 * k + 1]}; }
@@ -151,64 +153,223 @@ __device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 <
 // their side of the waits
 __device__ inline void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
 
+// units of a sequence: its full pages, plus one for a non-empty tail
+__device__ inline int units_of(int ctx, int max_pages) {
+  ctx = min(ctx, max_pages * kPage);
+  if (ctx <= 0) return 0;
+  return ctx / kPage + ((ctx % kPage) ? 1 : 0);
+}
+
+// P[b] = Hkv * sum_{b' < b} units(b'), P[B] = total units. One work-group.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __restrict__ ctx_lens,
+                                                          int32_t B, int32_t max_pages, int32_t hkv,
+                                                          int32_t* __restrict__ P) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  int32_t carry = 0;
+  for (int base = 0; base < B; base += 1024) {
+    const int b = base + t;
+    const int32_t v = (b < B) ? hkv * units_of(ctx_lens[b], max_pages) : 0;
+    part[t] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t x = (t >= off) ? part[t - off] : 0;
+      __syncthreads();
+      part[t] += x;
+      __syncthreads();
+    }
+    if (b < B) P[b] = carry + part[t] - v;
+    carry += part[1023];
+    __syncthreads();
+  }
+  if (t == 0) P[B] = carry;
+}
+
+// The wave that owns unit u when U units are split into W ranges
+// [w*U/W, (w+1)*U/W): the largest w with floor(w*U/W) <= u.
+__device__ __host__ inline int owner_wave(int64_t u, int64_t U, int W) {
+  return static_cast<int>(((u + 1) * W - 1) / U);
+}
+
+// Partial results: one slot of G x (128 outputs, m, l) floats per
+// (b*Hkv + h, wave) pair, at slot index (b*Hkv + h) + wave.
+constexpr int kSlotStride = kHeadDim + 2;
+
 template <int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ pages,
     const __half* __restrict__ tail_k, const __half* __restrict__ tail_v,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int32_t max_pages,
-    int32_t hkv, int32_t pps, int32_t max_splits, float sm_scale, float* __restrict__ ws_o,
-    float* __restrict__ ws_ml) {
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ P, int32_t B, int32_t max_pages, int32_t hkv, float sm_scale,
+    float* __restrict__ slots) {
   constexpr bool kPacked = (G <= 8);  // two pages share the logits B operand
   constexpr bool kPow2 = (G & (G - 1)) == 0;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int w = blockIdx.x, W = gridDim.x;
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
   const int hq = hkv * G;
 
-  // ctx is clamped to what the block table and the launch can address, so a
-  // broken precondition gives a wrong answer, never an out-of-bounds access.
-  const int ctx = min(ctx_lens[b], max_pages * kPage);
-  const int full = ctx > 0 ? ctx / kPage : 0;
-  const int tail_n = ctx > 0 ? ctx % kPage : 0;
-  const int nsplit = min(max_splits, max(1, (full + pps - 1) / pps));
-  if (split >= nsplit) return;
-  const int pbeg = split * pps;
-  const int pend = (split == nsplit - 1) ? min(full, pbeg + kMaxSplitPages) : min(full, pbeg + pps);
-  const int npg = max(0, pend - pbeg);
-  const bool do_tail = (split == nsplit - 1) && tail_n > 0;
+  const int64_t U = P[B];
+  const int64_t u0 = (int64_t)w * U / W;
+  const int64_t u1 = (int64_t)(w + 1) * U / W;
+  if (u0 >= u1) return;
+
+  // ---- locate the sequence holding unit u0: largest b with P[b] <= u0 ----
+  int b0 = 0;
+  {
+    int lo = 0, span = B;                  // search [lo, lo + span)
+    while (span > 1) {
+      const int step = (span + 63) / 64;
+      const int idx = lo + lane * step;
+      const bool le = (idx < lo + span) && (P[idx] <= u0);
+      const uint64_t m = __ballot(le);     // lanes are in increasing idx order
+      const int last = 63 - __builtin_clzll(m);   // lane 0 always qualifies
+      lo = lo + last * step;
+      span = min(step, B - lo);
+    }
+    b0 = __builtin_amdgcn_readfirstlane(lo);
+  }
 
   // Column roles. Packed: [0,G) = (head c, page A), [G,2G) = (head c-G, page B);
   // later columns mirror column c % G of page A so they stay finite.
   const int head = c % G;
   const int pslot = (kPacked && c >= G && c < 2 * G) ? 1 : 0;
   const bool lo_col = kPacked && c >= G && c < 2 * G;
-  // the lane holding the same head for the other page of the pair
   const int partner = kPacked ? (16 * g + ((c < G) ? c + G : (c < 2 * G ? c - G : c))) : lane;
   auto xchg = [&](float v) -> float {
     if constexpr (kPacked && kPow2) return __shfl_xor(v, G);
     else return __shfl(v, partner);
   };
-  const int my_head = h * G + head;  // query head of this lane's column
+  const float l2s = sm_scale * kLog2e;  // logits go to log2 units
+  const float qk_scale = l2s * kQkUnscale;
+  const int64_t page_stride = (int64_t)hkv * kChunkStride;
 
-  // Query in the logits B layout: element i of product m is channel 32m+8g+i,
-  // pre-scaled by 2^-4 (slots 0,1,4,5) or 2^-8 (slots 2,3,6,7).
-  h8 qc[4];
+  // ---- cursors over the wave's units (all fields wave-uniform) ----
+  struct Cursor {
+    int64_t u;   // flat index of the next unit
+    int b, h;    // sequence, KV head
+    int unit;    // unit inside (b, h)
+    int full;    // full pages of b
+    int nunits;  // units of b
+  };
+  auto seq_info = [&](int b, int& full, int& nunits) {
+    const int ctx = min(ctx_lens[b], max_pages * kPage);
+    full = ctx > 0 ? ctx / kPage : 0;
+    nunits = units_of(ctx, max_pages);
+  };
+  Cursor start;
   {
+    start.u = u0;
+    start.b = b0;
+    seq_info(b0, start.full, start.nunits);
+    const int64_t local = u0 - P[b0];
+    start.h = static_cast<int>(local / start.nunits);
+    start.unit = static_cast<int>(local % start.nunits);
+  }
+  // Entry at a cursor: a pair (or single) of pages, or the tail.
+  // Returns the number of units it covers (0 = tail).
+  auto entry_pages = [&](const Cursor& cu) -> int {
+    if (cu.unit >= cu.full) return 0;
+    return (cu.unit + 1 < cu.full && cu.u + 1 < u1) ? 2 : 1;
+  };
+  auto advance = [&](Cursor& cu, int n_units) {
+    cu.u += n_units;
+    cu.unit += n_units;
+    if (cu.unit >= cu.nunits && cu.u < u1) {
+      cu.unit = 0;
+      if (++cu.h == hkv) {
+        cu.h = 0;
+        do { ++cu.b; seq_info(cu.b, cu.full, cu.nunits); } while (cu.nunits == 0);
+      }
+    }
+  };
+
+  // ---- DMA ring ----
+  __shared__ __align__(16) uint8_t stage_s[kStages][kStageBytes];
+  __shared__ __align__(16) _Float16 tv_s[kPage][kHeadDim];
+  Cursor prod = start;
+  int issued = 0, consumed = 0;
+  // Issue the next pair of pages at the producer cursor (tails need no DMA).
+  auto produce = [&]() {
+    while (prod.u < u1 && entry_pages(prod) == 0) advance(prod, 1);
+    if (prod.u >= u1) return;
+    const int np = entry_pages(prod);
+    const int32_t* bt = block_table + (int64_t)prod.b * max_pages + prod.unit;
+    const int idA = bt[0];
+    const int idB = (np == 2) ? bt[1] : idA;
+    const int64_t head_off = (int64_t)prod.h * kChunkStride;
+    const uint8_t* chA = pages + idA * page_stride + head_off;
+    const uint8_t* chB = pages + idB * page_stride + head_off;
+    uint8_t* st = stage_s[issued % kStages];
+    dma16(chA + kOffKCodes + 16 * lane, st + 0);
+    dma16(chB + kOffKCodes + 16 * lane, st + 1024);
+    dma16(chA + kOffVCodes + 16 * lane, st + 2048);
+    dma16(chB + kOffVCodes + 16 * lane, st + 3072);
+    dma16((lane < 32 ? chA : chB) + kOffKScale + 16 * (lane & 31), st + 4096);
+    if (lane < 8) dma16((lane < 4 ? chA : chB) + kOffVScale + 16 * (lane & 3), st + 5120);
+    ++issued;
+    advance(prod, np);
+  };
+
+  // ---- per-(b, h) state ----
+  h8 qc[4];
+  float m_run = kNegInf, l_part = 0.f, lz_part = 0.f;
+  f4 o[8];
+  int cur_b = -1, cur_h = 0;
+
+  auto begin_segment = [&](int b, int h) {
+    cur_b = b;
+    cur_h = h;
+    const int my_head = h * G + head;
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + my_head) * kHeadDim);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      // element i of product m is channel 32m+8g+i, pre-scaled by 2^-4
+      // (slots 0,1,4,5) or 2^-8 (slots 2,3,6,7)
       const h8 v = as_h8(ld16(qrow + 2 * (32 * m + 8 * g)));
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         qc[m][i] = static_cast<_Float16>(static_cast<float>(v[i]) * (((i & 2) == 0) ? 0.0625f : 0.00390625f));
     }
-  }
-
-  const float l2s = sm_scale * kLog2e;  // logits go to log2 units
-  float m_run = kNegInf, l_part = 0.f, lz_part = 0.f;
-  f4 o[8];
+    m_run = kNegInf;
+    l_part = 0.f;
+    lz_part = 0.f;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  auto end_segment = [&]() {
+    if (cur_b < 0) return;
+    float l = l_part, lz = lz_part;
+    if constexpr (kPacked) {
+      // page-A and page-B lanes of a head each summed their own tokens
+      l += xchg(l);
+      lz += xchg(lz);
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    lz += __shfl_xor(lz, 16);
+    lz += __shfl_xor(lz, 32);
+    f4 ov[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      ov[t] = o[t];
+      if constexpr (kPacked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[t][i] += xchg(o[t][i]);
+      }
+    }
+    if (c < G) {
+      const int64_t slot = (int64_t)cur_b * hkv + cur_h + w;
+      float* dst = slots + (slot * G + c) * kSlotStride;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * t + 4 * g + i] = ov[t][i] * kPvUnscale + lz;
+      }
+      if (g == 0) { dst[kHeadDim] = m_run; dst[kHeadDim + 1] = l; }
+    }
+  };
 
   auto rescale_to = [&](float mb) {
     const float mnew = fmaxf(m_run, mb);
@@ -222,48 +383,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
   };
 
-  // ------------------------------------------------------------ int4 pages
-  // block ids of this split, one per lane (a split has at most 64 pages)
-  const int bt_lane = (lane < npg) ? block_table[(int64_t)b * max_pages + pbeg + lane] : 0;
-  const int64_t head_off = (int64_t)h * kChunkStride;
-  const int64_t page_stride = (int64_t)hkv * kChunkStride;
-  const float qk_scale = l2s * kQkUnscale;
-  const int npairs = (npg + 1) >> 1;
-
-  auto chunk_at = [&](int idx) -> const uint8_t* {
-    const int bid = __builtin_amdgcn_readlane(bt_lane, idx);
-    return pages + (int64_t)bid * page_stride + head_off;
-  };
-  __shared__ __align__(16) uint8_t stage_s[kStages][kStageBytes];
-
-  // Issue the DMA of pair i into its stage (block ids come from the lanes).
-  auto issue = [&](int i) {
-    const uint8_t* chA = chunk_at(2 * i);
-    const uint8_t* chB = chunk_at(min(2 * i + 1, npg - 1));
-    uint8_t* st = stage_s[i % kStages];
-    dma16(chA + kOffKCodes + 16 * lane, st + 0);
-    dma16(chB + kOffKCodes + 16 * lane, st + 1024);
-    dma16(chA + kOffVCodes + 16 * lane, st + 2048);
-    dma16(chB + kOffVCodes + 16 * lane, st + 3072);
-    dma16((lane < 32 ? chA : chB) + kOffKScale + 16 * (lane & 31), st + 4096);
-    if (lane < 8) dma16((lane < 4 ? chA : chB) + kOffVScale + 16 * (lane & 3), st + 5120);
-  };
-
-  if (npairs > 0) issue(0);
-  if (npairs > 1) issue(1);
-
-  // ------------------------------------------------------------ fp16 tail
-  // (processed while the first two page pairs are in flight)
-  if (do_tail) {
-    // the third stage is not written before the loop starts: stage the tail V there
-    _Float16 (*tv_s)[kHeadDim] = reinterpret_cast<_Float16 (*)[kHeadDim]>(&stage_s[kStages - 1][0]);
-    const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)b * hkv + h) * kPage * kHeadDim);
-    const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)b * hkv + h) * kPage * kHeadDim);
+  // ---- fp16 tail of (cur_b, cur_h): logits and output products on fp16 values
+  auto process_tail = [&]() {
+    const int ctx = min(ctx_lens[cur_b], max_pages * kPage);
+    const int tail_n = ctx % kPage;
+    const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
+    const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       reinterpret_cast<u4*>(&tv_s[0][0])[lane + 64 * i] = ld16(tv + 16 * (lane + 64 * i));
     // logits: A = K tail values (token c, channels 32m+8g..+8), B = plain q
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + my_head) * kHeadDim);
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((int64_t)cur_b * hq + cur_h * G + head) * kHeadDim);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -290,7 +421,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int i = 0; i < 4; ++i) l_part += p[i];
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     // output: A = V tail values of tokens 4g..4g+3 (slots 0..3), slots 4..7 empty
     h8 bhi, blo;
 #pragma unroll
@@ -301,6 +432,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       blo[i] = static_cast<_Float16>(x - static_cast<float>(xh));
     }
     const h8 bsel = lo_col ? blo : bhi;
+    f4 ot[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       h8 a;
@@ -309,22 +441,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         a[i] = (4 * g + i < tail_n) ? tv_s[4 * g + i][16 * t + c] : static_cast<_Float16>(0.f);
         a[4 + i] = static_cast<_Float16>(0.f);
       }
+      ot[t] = f4{0.f, 0.f, 0.f, 0.f};
       if constexpr (kPacked) {
-        o[t] = mfma(a, bsel, o[t]);
+        ot[t] = mfma(a, bsel, ot[t]);
       } else {
-        o[t] = mfma(a, bhi, o[t]);
-        o[t] = mfma(a, blo, o[t]);
+        ot[t] = mfma(a, bhi, ot[t]);
+        ot[t] = mfma(a, blo, ot[t]);
       }
+      // the pages' products carry 2^-24; bring the tail's to that scale (exact)
+      o[t] += ot[t] * (1.0f / kPvUnscale);
     }
-    // bring the tail's contribution to the page accumulators' scale (exact)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] *= (1.0f / kPvUnscale);
-  }
+    __builtin_amdgcn_wave_barrier();
+  };
 
-
-  auto process = [&](int i) {
-    const bool has_b = (2 * i + 1 < npg);
-    const uint8_t* st = stage_s[i % kStages];
+  // ---- one pair of pages from a ring stage ----
+  auto process_pair = [&](const uint8_t* st, bool has_b) {
     const u4 kcA = *reinterpret_cast<const u4*>(st + 16 * lane);
     const u4 kcB = *reinterpret_cast<const u4*>(st + 1024 + 16 * lane);
     const u4 vcA = *reinterpret_cast<const u4*>(st + 2048 + 16 * lane);
@@ -454,134 +585,130 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
   };
 
-  // Pipeline: pairs i+1 and i+2 are in flight (HBM -> LDS) while pair i is
-  // consumed. vmcnt counts this wave's outstanding vector-memory operations
-  // in issue order, so "at most 6 * (pairs issued after i)" means pair i has
-  // landed; nothing else in this loop touches vector memory.
-  for (int i = 0; i < npairs; ++i) {
-    wait_lgkmcnt0();   // the stage about to be refilled has been read out
-    compiler_fence();
-    if (i + 2 < npairs) {
-      issue(i + 2);
-      wait_vmcnt<2 * kDmaPerStage>();
-    } else if (i + 1 < npairs) {
-      wait_vmcnt<kDmaPerStage>();
+  // ---- main stream ----
+  // Pairs are issued two ahead of the one consumed. vmcnt counts this wave's
+  // outstanding vector-memory operations in issue order, so "at most 6 x
+  // (pairs issued after this one)" means this pair has landed in LDS; other
+  // vector loads (query, tail) only add younger operations, which makes the
+  // wait stricter, never looser.
+  produce();
+  produce();
+  Cursor cons = start;
+  while (cons.u < u1) {
+    if (cons.b != cur_b || cons.h != cur_h) {
+      end_segment();
+      begin_segment(cons.b, cons.h);
+    }
+    const int np = entry_pages(cons);
+    if (np > 0) {
+      wait_lgkmcnt0();  // the stage about to be refilled has been read out
+      compiler_fence();
+      produce();
+      const int after = issued - consumed - 1;
+      if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
+      else if (after == 1) wait_vmcnt<kDmaPerStage>();
+      else wait_vmcnt<0>();
+      compiler_fence();
+      process_pair(stage_s[consumed % kStages], np == 2);
+      compiler_fence();
+      ++consumed;
+      advance(cons, np);
     } else {
-      wait_vmcnt<0>();
+      process_tail();
+      advance(cons, 1);
     }
-    compiler_fence();
-    process(i);
-    compiler_fence();
   }
-
-  // ------------------------------------------------------------ write partials
-  if constexpr (kPacked) {
-    // page-A and page-B lanes of a head each summed their own tokens
-    l_part += xchg(l_part);
-    lz_part += xchg(lz_part);
-  }
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
-  lz_part += __shfl_xor(lz_part, 16);
-  lz_part += __shfl_xor(lz_part, 32);
-  if constexpr (kPacked) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[t][i] += xchg(o[t][i]);
-  }
-  if (c < G) {
-    const int64_t row = ((int64_t)b * hq + h * G + c) * max_splits + split;
-    float* dst = ws_o + row * kHeadDim;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      f4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = o[t][i] * kPvUnscale + lz_part;
-      *reinterpret_cast<f4*>(dst + 16 * t + 4 * g) = v;
-    }
-    if (g == 0) { ws_ml[2 * row] = m_run; ws_ml[2 * row + 1] = l_part; }
-  }
+  end_segment();
 }
 
-// Merge the splits of (sequence, query head), m in log2 units:
+// Merge, for (sequence b, query head j), the partial results of the waves
+// whose unit ranges touched (b, j / G); m in log2 units:
 // M = max m_s, O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 __global__ __launch_bounds__(128) void splitk_reduce_kernel(
-    const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-    const int32_t* __restrict__ ctx_lens, int32_t max_pages, int32_t hq, int32_t pps,
-    int32_t max_splits, __half* __restrict__ out) {
+    const float* __restrict__ slots, const int32_t* __restrict__ P,
+    const int32_t* __restrict__ ctx_lens, int32_t B, int32_t max_pages, int32_t hkv, int32_t G,
+    int32_t W, __half* __restrict__ out) {
   const int j = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int ctx = min(ctx_lens[b], max_pages * kPage);
+  const int hq = hkv * G;
+  const int h = j / G, jj = j % G;
   __half* o = out + ((int64_t)b * hq + j) * kHeadDim;
-  if (ctx <= 0) { o[d] = __float2half(0.f); return; }
-  const int full = ctx / kPage;
-  const int nsplit = min(max_splits, max(1, (full + pps - 1) / pps));
-  const int64_t row0 = ((int64_t)b * hq + j) * max_splits;
+  const int n = units_of(ctx_lens[b], max_pages);
+  const int64_t U = P[B];
+  if (n <= 0 || U <= 0) { o[d] = __float2half(0.f); return; }
+  const int64_t ustart = (int64_t)P[b] + (int64_t)h * n;
+  const int wf = owner_wave(ustart, U, W);
+  const int wl = owner_wave(ustart + n - 1, U, W);
+  const int64_t bh = (int64_t)b * hkv + h;
+  // waves strictly between two owners can have empty ranges (when U < W);
+  // they wrote nothing
+  auto empty = [&](int wv) { return (int64_t)wv * U / W == (int64_t)(wv + 1) * U / W; };
   float mx = kNegInf;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, ws_ml[2 * (row0 + s)]);
+  for (int wv = wf; wv <= wl; ++wv)
+    if (!empty(wv)) mx = fmaxf(mx, slots[((bh + wv) * G + jj) * kSlotStride + kHeadDim]);
   float den = 0.f, num = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = ws_ml[2 * (row0 + s)];
-    const float w = (ms == kNegInf) ? 0.f : exp2f(ms - mx);
-    den += w * ws_ml[2 * (row0 + s) + 1];
-    num += w * ws_o[(row0 + s) * kHeadDim + d];
+  for (int wv = wf; wv <= wl; ++wv) {
+    if (empty(wv)) continue;
+    const float* sl = slots + ((bh + wv) * G + jj) * kSlotStride;
+    const float ms = sl[kHeadDim];
+    const float wt = (ms == kNegInf) ? 0.f : exp2f(ms - mx);
+    den += wt * sl[kHeadDim + 1];
+    num += wt * sl[d];
   }
   o[d] = __float2half_rn(num / den);
 }
 
+int resident_waves() {
+  // one wave per work-group, two per SIMD, four SIMDs per CU
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached = cus * 8;
+    if (cached > kMaxWaves) cached = kMaxWaves;
+  }
+  return cached;
+}
+
+size_t p_bytes(const s4kv_shape& s) { return ((size_t)(s.num_seqs + 1) * 4 + 255) & ~size_t(255); }
+
 template <int G>
-hipError_t launch_g(const s4kv_shape& s, const SplitPlan& plan, const void* q, const void* pages,
+hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages,
                     const void* tail_k, const void* tail_v, const int32_t* block_table,
-                    const int32_t* ctx_lens, float sm_scale, float* ws_o, float* ws_ml,
+                    const int32_t* ctx_lens, const int32_t* P, float sm_scale, float* slots,
                     hipStream_t stream) {
-  dim3 grid(plan.max_splits, s.num_kv_heads, s.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(64), 0, stream,
+  hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(W), dim3(64), 0, stream,
                      static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
                      static_cast<const __half*>(tail_k), static_cast<const __half*>(tail_v),
-                     block_table, ctx_lens, s.max_pages_per_seq, s.num_kv_heads,
-                     plan.pages_per_split, plan.max_splits, sm_scale, ws_o, ws_ml);
+                     block_table, ctx_lens, P, s.num_seqs, s.max_pages_per_seq, s.num_kv_heads,
+                     sm_scale, slots);
   return hipGetLastError();
 }
 
 }  // namespace
 
-SplitPlan plan_splits(const s4kv_shape& s, int32_t max_ctx) {
-  const int64_t max_full = max_ctx / kPage;
-  // Aim for about 8192 work-groups over the whole batch when every sequence
-  // is at max_ctx; 8 to 64 pages per work-group (the block ids of a split sit
-  // one per lane); an even count so pages pair up inside a split.
-  const int64_t work = (int64_t)s.num_seqs * s.num_kv_heads * max_full;
-  int64_t pps = (work + 8191) / 8192;
-  if (pps < 8) pps = 8;
-  if (pps > kMaxSplitPages) pps = kMaxSplitPages;
-  pps = (pps + 1) & ~int64_t(1);
-  SplitPlan p;
-  p.pages_per_split = static_cast<int>(pps);
-  p.max_splits = static_cast<int>(max_full > 0 ? (max_full + pps - 1) / pps : 1);
-  if (p.max_splits < 1) p.max_splits = 1;
-  return p;
+size_t workspace_bytes(const s4kv_shape& s) {
+  const size_t nslots = (size_t)s.num_seqs * s.num_kv_heads + kMaxWaves;
+  const int G = s.num_q_heads / s.num_kv_heads;
+  return p_bytes(s) + nslots * G * kSlotStride * sizeof(float);
 }
 
-size_t workspace_bytes(const s4kv_shape& s, const SplitPlan& plan) {
-  const size_t rows = (size_t)s.num_seqs * s.num_q_heads * plan.max_splits;
-  size_t o_bytes = rows * kHeadDim * sizeof(float);
-  o_bytes = (o_bytes + 255) & ~size_t(255);
-  return o_bytes + rows * 2 * sizeof(float);
-}
-
-hipError_t launch_paged_decode(const s4kv_shape& s, const SplitPlan& plan, const void* q,
-                               const void* pages, const void* tail_k, const void* tail_v,
+hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* pages,
+                               const void* tail_k, const void* tail_v,
                                const int32_t* block_table, const int32_t* ctx_lens,
                                float sm_scale, void* out, void* workspace, hipStream_t stream) {
-  const size_t rows = (size_t)s.num_seqs * s.num_q_heads * plan.max_splits;
-  size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~size_t(255);
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  int32_t* P = static_cast<int32_t*>(workspace);
+  float* slots = reinterpret_cast<float*>(static_cast<char*>(workspace) + p_bytes(s));
+  const int W = resident_waves();
   const int G = s.num_q_heads / s.num_kv_heads;
-  hipError_t e = hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, ctx_lens, s.num_seqs,
+                     s.max_pages_per_seq, s.num_kv_heads, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   switch (G) {
 #define S4KV_CASE(g) \
-  case g: e = launch_g<g>(s, plan, q, pages, tail_k, tail_v, block_table, ctx_lens, sm_scale, ws_o, ws_ml, stream); break;
+  case g: e = launch_g<g>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, P, sm_scale, slots, stream); break;
     S4KV_CASE(1) S4KV_CASE(2) S4KV_CASE(3) S4KV_CASE(4) S4KV_CASE(5) S4KV_CASE(6) S4KV_CASE(7)
     S4KV_CASE(8) S4KV_CASE(9) S4KV_CASE(10) S4KV_CASE(11) S4KV_CASE(12) S4KV_CASE(13)
     S4KV_CASE(14) S4KV_CASE(15) S4KV_CASE(16)
@@ -590,8 +717,8 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const SplitPlan& plan, const
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_q_heads, s.num_seqs), dim3(kHeadDim), 0,
-                     stream, ws_o, ws_ml, ctx_lens, s.max_pages_per_seq, s.num_q_heads,
-                     plan.pages_per_split, plan.max_splits, static_cast<__half*>(out));
+                     stream, slots, P, ctx_lens, s.num_seqs, s.max_pages_per_seq, s.num_kv_heads,
+                     G, W, static_cast<__half*>(out));
   return hipGetLastError();
 }
 
