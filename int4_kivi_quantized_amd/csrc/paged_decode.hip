@@ -153,6 +153,66 @@ __device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 <
 // their side of the waits
 __device__ inline void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
 
+// The stage a pair occupies, read into registers. The reads are one asm block
+// that ends with its own lgkmcnt(0): the compiler cannot see which LDS bytes
+// the DMA writes, and for compiler-visible LDS loads it would wait for every
+// outstanding DMA, draining the ring; here the caller's explicit vmcnt wait is
+// the only guard, and every output is complete when the block ends.
+struct Stage {
+  u4 kcA, kcB, vcA, vcB;     // K / V codes of pages A and B (this lane's 16 bytes)
+  u2 svA, zvA, svB, zvB;     // V scale / zero of tokens 4g..4g+3
+  u4 sc[4], ze[4];           // K scale / zero of this lane's 32 channels, one page
+};
+
+// base: LDS address of the stage; page: whose K scale/zero block to read
+__device__ inline void read_stage(uint32_t base, int lane, int g, int page, Stage& r) {
+  const uint32_t a_lane = base + 16 * lane;
+  const uint32_t a_v = base + 8 * g;
+  const uint32_t a_k = base + 512 * page + 16 * g;
+  __asm__ __volatile__(
+      "ds_read_b128 %0, %16\n\t"
+      "ds_read_b128 %1, %16 offset:1024\n\t"
+      "ds_read_b128 %2, %16 offset:2048\n\t"
+      "ds_read_b128 %3, %16 offset:3072\n\t"
+      "ds_read_b64 %4, %17 offset:5120\n\t"
+      "ds_read_b64 %5, %17 offset:5152\n\t"
+      "ds_read_b64 %6, %17 offset:5184\n\t"
+      "ds_read_b64 %7, %17 offset:5216\n\t"
+      "ds_read_b128 %8, %18 offset:4096\n\t"
+      "ds_read_b128 %9, %18 offset:4160\n\t"
+      "ds_read_b128 %10, %18 offset:4224\n\t"
+      "ds_read_b128 %11, %18 offset:4288\n\t"
+      "ds_read_b128 %12, %18 offset:4352\n\t"
+      "ds_read_b128 %13, %18 offset:4416\n\t"
+      "ds_read_b128 %14, %18 offset:4480\n\t"
+      "ds_read_b128 %15, %18 offset:4544\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.kcA), "=&v"(r.kcB), "=&v"(r.vcA), "=&v"(r.vcB), "=&v"(r.svA), "=&v"(r.zvA),
+        "=&v"(r.svB), "=&v"(r.zvB), "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]),
+        "=&v"(r.sc[3]), "=&v"(r.ze[0]), "=&v"(r.ze[1]), "=&v"(r.ze[2]), "=&v"(r.ze[3])
+      : "v"(a_lane), "v"(a_v), "v"(a_k)
+      : "memory");
+}
+
+// K scale / zero of one more page (wide groups read both pages)
+__device__ inline void read_kmeta(uint32_t base, int g, int page, u4 (&sc)[4], u4 (&ze)[4]) {
+  const uint32_t a_k = base + 512 * page + 16 * g;
+  __asm__ __volatile__(
+      "ds_read_b128 %0, %8 offset:4096\n\t"
+      "ds_read_b128 %1, %8 offset:4160\n\t"
+      "ds_read_b128 %2, %8 offset:4224\n\t"
+      "ds_read_b128 %3, %8 offset:4288\n\t"
+      "ds_read_b128 %4, %8 offset:4352\n\t"
+      "ds_read_b128 %5, %8 offset:4416\n\t"
+      "ds_read_b128 %6, %8 offset:4480\n\t"
+      "ds_read_b128 %7, %8 offset:4544\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3]), "=&v"(ze[0]), "=&v"(ze[1]),
+        "=&v"(ze[2]), "=&v"(ze[3])
+      : "v"(a_k)
+      : "memory");
+}
+
 // units of a sequence: its full pages, plus one for a non-empty tail
 __device__ inline int units_of(int ctx, int max_pages) {
   ctx = min(ctx, max_pages * kPage);
@@ -455,34 +515,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   // ---- one pair of pages from a ring stage ----
+  auto lds_addr = [&](const uint8_t* p) -> uint32_t {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint8_t*)(p)));
+  };
   auto process_pair = [&](const uint8_t* st, bool has_b) {
-    const u4 kcA = *reinterpret_cast<const u4*>(st + 16 * lane);
-    const u4 kcB = *reinterpret_cast<const u4*>(st + 1024 + 16 * lane);
-    const u4 vcA = *reinterpret_cast<const u4*>(st + 2048 + 16 * lane);
-    const u4 vcB = *reinterpret_cast<const u4*>(st + 3072 + 16 * lane);
-    const u2 svA = *reinterpret_cast<const u2*>(st + 5120 + 8 * g);
-    const u2 zvA = *reinterpret_cast<const u2*>(st + 5120 + 32 + 8 * g);
-    const u2 svB = *reinterpret_cast<const u2*>(st + 5184 + 8 * g);
-    const u2 zvB = *reinterpret_cast<const u2*>(st + 5184 + 32 + 8 * g);
-    auto kmeta_read = [&](int page, u4 (&sc)[4], u4 (&ze)[4]) {
-      const uint8_t* km = st + 4096 + 512 * page;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        sc[m] = *reinterpret_cast<const u4*>(km + 64 * m + 16 * g);        // scale, ch 32m+8g..
-        ze[m] = *reinterpret_cast<const u4*>(km + 256 + 64 * m + 16 * g);  // zero, same channels
-      }
-    };
+    Stage r;
+    read_stage(lds_addr(st), lane, g, kPacked ? pslot : 0, r);
+    const u4 kcA = r.kcA, kcB = r.kcB, vcA = r.vcA, vcB = r.vcB;
+    const u2 svA = r.svA, zvA = r.zvA, svB = r.svB, zvB = r.zvB;
     // ---- logits ----
     f4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
     float lgA[4], lgB[4];
     float p_own[4], pA[4], pB[4];
     if constexpr (kPacked) {
-      u4 sc[4], ze[4];
-      kmeta_read(pslot, sc, ze);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
-        qs_split(qc[m], sc[m], hi, lo);
+        qs_split(qc[m], r.sc[m], hi, lo);
         const h8 ka = k_operand(kcA[m]);
         const h8 kb = k_operand(kcB[m]);
         accA = mfma(ka, hi, accA);
@@ -490,7 +540,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      float zt = zero_term(qc, ze);
+      float zt = zero_term(qc, r.ze);
       zt += __shfl_xor(zt, 16);
       zt += __shfl_xor(zt, 32);
       const float zl = zt * l2s;
@@ -518,13 +568,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         pB[k] = pslot ? p_own[k] : other;
       }
     } else {
-      u4 scA[4], zeA[4], scB[4], zeB[4];
-      kmeta_read(0, scA, zeA);
-      kmeta_read(1, scB, zeB);
+      u4 scB[4], zeB[4];
+      read_kmeta(lds_addr(st), g, 1, scB, zeB);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
-        qs_split(qc[m], scA[m], hi, lo);
+        qs_split(qc[m], r.sc[m], hi, lo);
         const h8 ka = k_operand(kcA[m]);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
@@ -533,7 +582,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      float zA = zero_term(qc, zeA);
+      float zA = zero_term(qc, r.ze);
       zA += __shfl_xor(zA, 16);
       zA += __shfl_xor(zA, 32);
       float zB = zero_term(qc, zeB);
