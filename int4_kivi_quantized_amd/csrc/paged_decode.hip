@@ -253,7 +253,7 @@ __device__ __host__ inline int owner_wave(int64_t u, int64_t U, int W) {
 
 // Partial results: one slot of G x (128 outputs, m, l) floats per
 // (b*Hkv + h, wave) pair, at slot index (b*Hkv + h) + wave.
-constexpr int kSlotStride = kHeadDim + 2;
+constexpr int kSlotStride = kHeadDim + 4;  // 128 outputs, m, l, 2 pad (16-byte rows)
 
 template <int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
@@ -349,6 +349,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   __shared__ __align__(16) _Float16 tv_s[kPage][kHeadDim];
   Cursor prod = start;
   int issued = 0, consumed = 0;
+  auto q_row = [&](int b, int h) {
+    return reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + h * G + head) * kHeadDim);
+  };
   // Issue the next pair of pages at the producer cursor (tails need no DMA).
   auto produce = [&]() {
     while (prod.u < u1 && entry_pages(prod) == 0) advance(prod, 1);
@@ -380,13 +383,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   auto begin_segment = [&](int b, int h) {
     cur_b = b;
     cur_h = h;
-    const int my_head = h * G + head;
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + my_head) * kHeadDim);
+    // the query of the new (b, h); loading it waits for the ring's DMAs,
+    // once per segment
+    u4 raw[4];
+    const uint8_t* qr = q_row(b, h);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) raw[m] = ld16(qr + 2 * (32 * m + 8 * g));
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // element i of product m is channel 32m+8g+i, pre-scaled by 2^-4
       // (slots 0,1,4,5) or 2^-8 (slots 2,3,6,7)
-      const h8 v = as_h8(ld16(qrow + 2 * (32 * m + 8 * g)));
+      const h8 v = as_h8(raw[m]);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         qc[m][i] = static_cast<_Float16>(static_cast<float>(v[i]) * (((i & 2) == 0) ? 0.0625f : 0.00390625f));
@@ -424,8 +431,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       float* dst = slots + (slot * G + c) * kSlotStride;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
+        f4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[16 * t + 4 * g + i] = ov[t][i] * kPvUnscale + lz;
+        for (int i = 0; i < 4; ++i) v[i] = ov[t][i] * kPvUnscale + lz;
+        *reinterpret_cast<f4*>(dst + 16 * t + 4 * g) = v;
       }
       if (g == 0) { dst[kHeadDim] = m_run; dst[kHeadDim + 1] = l; }
     }
@@ -454,7 +463,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int i = 0; i < 4; ++i)
       reinterpret_cast<u4*>(&tv_s[0][0])[lane + 64 * i] = ld16(tv + 16 * (lane + 64 * i));
     // logits: A = K tail values (token c, channels 32m+8g..+8), B = plain q
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((int64_t)cur_b * hq + cur_h * G + head) * kHeadDim);
+    const uint8_t* qrow = q_row(cur_b, cur_h);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -670,40 +679,52 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   end_segment();
 }
 
-// Merge, for (sequence b, query head j), the partial results of the waves
-// whose unit ranges touched (b, j / G); m in log2 units:
-// M = max m_s, O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-__global__ __launch_bounds__(128) void splitk_reduce_kernel(
+// Merge, for (sequence b, KV head h), the partial results of the waves whose
+// unit ranges touched (b, h): an online merge over the slots, m in log2 units,
+// O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M the running max.
+// Block: 32 threads per query head of the group, 4 outputs per thread.
+__global__ __launch_bounds__(512) void splitk_reduce_kernel(
     const float* __restrict__ slots, const int32_t* __restrict__ P,
     const int32_t* __restrict__ ctx_lens, int32_t B, int32_t max_pages, int32_t hkv, int32_t G,
     int32_t W, __half* __restrict__ out) {
-  const int j = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int jj = threadIdx.x >> 5, d0 = 4 * (threadIdx.x & 31);
   const int hq = hkv * G;
-  const int h = j / G, jj = j % G;
-  __half* o = out + ((int64_t)b * hq + j) * kHeadDim;
+  __half* o = out + ((int64_t)b * hq + h * G + jj) * kHeadDim + d0;
   const int n = units_of(ctx_lens[b], max_pages);
   const int64_t U = P[B];
-  if (n <= 0 || U <= 0) { o[d] = __float2half(0.f); return; }
+  if (n <= 0 || U <= 0) {
+    *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
   const int64_t ustart = (int64_t)P[b] + (int64_t)h * n;
   const int wf = owner_wave(ustart, U, W);
   const int wl = owner_wave(ustart + n - 1, U, W);
   const int64_t bh = (int64_t)b * hkv + h;
-  // waves strictly between two owners can have empty ranges (when U < W);
-  // they wrote nothing
-  auto empty = [&](int wv) { return (int64_t)wv * U / W == (int64_t)(wv + 1) * U / W; };
-  float mx = kNegInf;
-  for (int wv = wf; wv <= wl; ++wv)
-    if (!empty(wv)) mx = fmaxf(mx, slots[((bh + wv) * G + jj) * kSlotStride + kHeadDim]);
-  float den = 0.f, num = 0.f;
+  float M = kNegInf, L = 0.f;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int wv = wf; wv <= wl; ++wv) {
-    if (empty(wv)) continue;
+    // waves strictly between two owners can have empty ranges (when U < W);
+    // they wrote nothing
+    if ((int64_t)wv * U / W == (int64_t)(wv + 1) * U / W) continue;
     const float* sl = slots + ((bh + wv) * G + jj) * kSlotStride;
-    const float ms = sl[kHeadDim];
-    const float wt = (ms == kNegInf) ? 0.f : exp2f(ms - mx);
-    den += wt * sl[kHeadDim + 1];
-    num += wt * sl[d];
+    const float ms = sl[kHeadDim], ls = sl[kHeadDim + 1];
+    const f4 os = *reinterpret_cast<const f4*>(sl + d0);
+    if (ms == kNegInf) continue;
+    const float Mn = fmaxf(M, ms);
+    const float a = (M == kNegInf) ? 0.f : exp2f(M - Mn);
+    const float c = exp2f(ms - Mn);
+    L = L * a + ls * c;
+    acc = acc * a + os * c;
+    M = Mn;
   }
-  o[d] = __float2half_rn(num / den);
+  const float inv = 1.0f / L;
+  __half2 lo = __floats2half2_rn(acc[0] * inv, acc[1] * inv);
+  __half2 hi = __floats2half2_rn(acc[2] * inv, acc[3] * inv);
+  uint2 pk;
+  pk.x = *reinterpret_cast<uint32_t*>(&lo);
+  pk.y = *reinterpret_cast<uint32_t*>(&hi);
+  *reinterpret_cast<uint2*>(o) = pk;
 }
 
 int resident_waves() {
@@ -765,7 +786,7 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_q_heads, s.num_seqs), dim3(kHeadDim), 0,
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads, s.num_seqs), dim3(32 * G), 0,
                      stream, slots, P, ctx_lens, s.num_seqs, s.max_pages_per_seq, s.num_kv_heads,
                      G, W, static_cast<__half*>(out));
   return hipGetLastError();
