@@ -98,6 +98,49 @@ __device__ inline _Float16 h_at2(u2 v, int i) {
   return __builtin_bit_cast(h2v, (uint32_t)v[i >> 1])[i & 1];
 }
 
+// ---- cross-lane steps on the VALU (no LDS round trip) ----
+__device__ inline uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ inline float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
+// v from lane l ^ 16 and from lane l ^ 32 combined with v itself (sum / max
+// over the four 16-lane rows): permlane16_swap pairs rows 0-1 and 2-3,
+// permlane32_swap pairs the two halves of the wave.
+__device__ inline float rows_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+  v = bitsf(r[0]) + bitsf(r[1]);
+  auto t = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+  return bitsf(t[0]) + bitsf(t[1]);
+}
+__device__ inline float rows_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+  v = fmaxf(bitsf(r[0]), bitsf(r[1]));
+  auto t = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+  return fmaxf(bitsf(t[0]), bitsf(t[1]));
+}
+// DPP controls (within rows of 16 lanes)
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowRor4 = 0x124;    // row_ror:4  (lane c <- c-4 mod 16)
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8  (lane c <- c^8)
+constexpr int kDppRowRor12 = 0x12C;   // row_ror:12 (lane c <- c+4 mod 16)
+template <int Ctrl>
+__device__ inline float dpp(float v) {
+  return bitsf(static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(fbits(v)), Ctrl, 0xF, 0xF, false)));
+}
+// The value of the lane holding the same head for the other page of a pair
+// (column c +- G for G <= 8). Power-of-two groups use DPP; others bpermute.
+template <int G>
+__device__ inline float pair_partner(float v, int c, int partner_lane) {
+  if constexpr (G == 1) return dpp<kDppQuadSwap1>(v);
+  else if constexpr (G == 2) return dpp<kDppQuadSwap2>(v);
+  else if constexpr (G == 4) {
+    const float up = dpp<kDppRowRor12>(v);   // from c + 4
+    const float dn = dpp<kDppRowRor4>(v);    // from c - 4
+    return (c & 4) ? dn : up;
+  } else if constexpr (G == 8) return dpp<kDppRowRor8>(v);
+  else return __shfl(v, partner_lane);
+}
+
 // qs = qc * s as an fp16 (hi, lo) pair for the 8 elements of one product,
 // two elements per packed fp16 instruction: hi = fp16(qc*s) (one rounding of
 // the exact product) and lo = fma(qc, s, -hi) (exact product minus hi, one
@@ -263,7 +306,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int32_t* __restrict__ P, int32_t B, int32_t max_pages, int32_t hkv, float sm_scale,
     float* __restrict__ slots) {
   constexpr bool kPacked = (G <= 8);  // two pages share the logits B operand
-  constexpr bool kPow2 = (G & (G - 1)) == 0;
   const int w = blockIdx.x, W = gridDim.x;
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
@@ -296,10 +338,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int pslot = (kPacked && c >= G && c < 2 * G) ? 1 : 0;
   const bool lo_col = kPacked && c >= G && c < 2 * G;
   const int partner = kPacked ? (16 * g + ((c < G) ? c + G : (c < 2 * G ? c - G : c))) : lane;
-  auto xchg = [&](float v) -> float {
-    if constexpr (kPacked && kPow2) return __shfl_xor(v, G);
-    else return __shfl(v, partner);
-  };
+  auto xchg = [&](float v) -> float { return pair_partner<G>(v, c, partner); };
   const float l2s = sm_scale * kLog2e;  // logits go to log2 units
   const float qk_scale = l2s * kQkUnscale;
   const int64_t page_stride = (int64_t)hkv * kChunkStride;
@@ -346,20 +385,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // ---- DMA ring ----
   __shared__ __align__(16) uint8_t stage_s[kStages][kStageBytes];
-  __shared__ __align__(16) _Float16 tv_s[kPage][kHeadDim];
   Cursor prod = start;
   int issued = 0, consumed = 0;
   auto q_row = [&](int b, int h) {
     return reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + h * G + head) * kHeadDim);
   };
-  // Issue the next pair of pages at the producer cursor (tails need no DMA).
+  // Block ids of the pair at the producer cursor, loaded one pair ahead of
+  // their use so the scalar-load latency overlaps a whole iteration.
+  auto next_pair = [&](Cursor& cu) -> bool {
+    while (cu.u < u1 && entry_pages(cu) == 0) advance(cu, 1);
+    return cu.u < u1;
+  };
+  int nid_a = 0, nid_b = 0;
+  auto prefetch_ids = [&]() {
+    if (!next_pair(prod)) return;
+    const int32_t* bt = block_table + (int64_t)prod.b * max_pages + prod.unit;
+    nid_a = bt[0];
+    nid_b = (entry_pages(prod) == 2) ? bt[1] : nid_a;
+  };
+  // Issue the pair at the producer cursor (tails need no DMA).
   auto produce = [&]() {
-    while (prod.u < u1 && entry_pages(prod) == 0) advance(prod, 1);
     if (prod.u >= u1) return;
     const int np = entry_pages(prod);
-    const int32_t* bt = block_table + (int64_t)prod.b * max_pages + prod.unit;
-    const int idA = bt[0];
-    const int idB = (np == 2) ? bt[1] : idA;
+    const int idA = nid_a, idB = nid_b;
     const int64_t head_off = (int64_t)prod.h * kChunkStride;
     const uint8_t* chA = pages + idA * page_stride + head_off;
     const uint8_t* chB = pages + idB * page_stride + head_off;
@@ -372,6 +420,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (lane < 8) dma16((lane < 4 ? chA : chB) + kOffVScale + 16 * (lane & 3), st + 5120);
     ++issued;
     advance(prod, np);
+    prefetch_ids();
   };
 
   // ---- per-(b, h) state ----
@@ -413,10 +462,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       l += xchg(l);
       lz += xchg(lz);
     }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    lz += __shfl_xor(lz, 16);
-    lz += __shfl_xor(lz, 32);
+    l = rows_sum(l);
+    lz = rows_sum(lz);
     f4 ov[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -458,6 +505,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int tail_n = ctx % kPage;
     const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
     const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
+    // Stage the tail V in the ring slot the producer fills next: between two
+    // pairs at most kStages-1 pairs are in flight, so that slot is free.
+    _Float16 (*tv_s)[kHeadDim] = reinterpret_cast<_Float16 (*)[kHeadDim]>(&stage_s[issued % kStages][0]);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -479,8 +529,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       lg[i] = (4 * g + i < tail_n) ? acc[i] * l2s : kNegInf;
       mb = fmaxf(mb, lg[i]);
     }
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mb = rows_max(mb);
     rescale_to(mb);
     float p[4];
 #pragma unroll
@@ -549,9 +598,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      float zt = zero_term(qc, r.ze);
-      zt += __shfl_xor(zt, 16);
-      zt += __shfl_xor(zt, 32);
+      const float zt = rows_sum(zero_term(qc, r.ze));
       const float zl = zt * l2s;
       const f4 mine = pslot ? accB : accA;
       const bool valid = !(pslot && !has_b);
@@ -561,8 +608,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         lgA[k] = valid ? mine[k] * qk_scale + zl : kNegInf;
         mb = fmaxf(mb, lgA[k]);
       }
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      mb = rows_max(mb);
       mb = fmaxf(mb, xchg(mb));
       rescale_to(mb);
 #pragma unroll
@@ -591,12 +637,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      float zA = zero_term(qc, r.ze);
-      zA += __shfl_xor(zA, 16);
-      zA += __shfl_xor(zA, 32);
-      float zB = zero_term(qc, zeB);
-      zB += __shfl_xor(zB, 16);
-      zB += __shfl_xor(zB, 32);
+      const float zA = rows_sum(zero_term(qc, r.ze));
+      const float zB = rows_sum(zero_term(qc, zeB));
       float mb = kNegInf;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -604,8 +646,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         lgB[k] = has_b ? accB[k] * qk_scale + zB * l2s : kNegInf;
         mb = fmaxf(mb, fmaxf(lgA[k], lgB[k]));
       }
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      mb = rows_max(mb);
       rescale_to(mb);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -649,6 +690,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // (pairs issued after this one)" means this pair has landed in LDS; other
   // vector loads (query, tail) only add younger operations, which makes the
   // wait stricter, never looser.
+  prefetch_ids();
   produce();
   produce();
   Cursor cons = start;
