@@ -1,0 +1,56 @@
+"""Byte accounting pinned to the figures the pages print (tests/golden/page_figures.json).
+
+The fp16 payload formula is the one the FP8 KV-cache capacity guide gives
+(adechristanto.de, section on separating weights, running state and reserved
+memory); the int4 page size follows from the page format. Both feed the GB/s
+that bench.py reports, so they are checked against the pages' own numbers.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from workload import accounting as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def _figures():
+    with open(GOLDEN) as f:
+        return {g["name"]: g for g in json.load(f)["figures"]}
+
+
+@pytest.mark.parametrize("name", ["fp16_kv_per_sequence_llama31_70b_4096",
+                                  "fp16_kv_per_request_llama3_70b_32k",
+                                  "fp16_kv_256_sequences_llama31_70b_4096"])
+def test_fp16_payload_matches_printed_figures(name):
+    g = _figures()[name]
+    got = A.fp16_kv_bytes(g["layers"], g["kv_heads"], g["head_dim"], g["tokens"], g["bytes_per_elem"])
+    assert g["lo"] <= got <= g["hi"], (name, got)
+
+
+def test_int4_density_matches_printed_figure():
+    g = _figures()["int4_kivi_density_vs_fp16"]
+    d = A.density_vs_fp16()
+    assert g["lo"] <= d <= g["hi"]
+    # 164 B per token per KV head: codes 64 + 64, V scale/zero 4, K scale/zero 512 / 16
+    assert A.int4_bytes_per_token_per_head() == 64 + 64 + 4 + 32
+    assert A.CHUNK_BYTES == 2624
+
+
+def test_cache_bytes_counts_pages_and_tail():
+    # 37 tokens = 2 full pages + 5 tail tokens, per KV head
+    assert A.cache_bytes([37], 3) == 3 * (2 * 2624 + 5 * 512)
+    assert A.cache_bytes([16, 0, 15], 1) == 2624 + 15 * 512
+    # decode bytes add block-table entries, ctx lengths, Q and O
+    b = A.decode_bytes(np.array([37]), 12, 3)
+    assert b == A.cache_bytes([37], 3) + 4 * 2 + 4 + 2 * (2 * 12 * 128)
+
+
+def test_llama3_70b_layout_total():
+    # 16 sequences x 32768 tokens x 8 KV heads x 80 layers at 164 B per token-head
+    per_layer = A.cache_bytes(np.full(16, 32768), 8)
+    assert per_layer == 16 * 8 * 2048 * 2624
+    assert abs(80 * per_layer / 1e9 - 55.03) < 0.01
