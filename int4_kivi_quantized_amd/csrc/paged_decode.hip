@@ -24,13 +24,16 @@
 //  * logits, transposed: S^T[token][col] = sum_d codeK[token][d] * qs[d][col]
 //    with qs = q * sK (the per-channel K scale folded into the query, per page)
 //    plus the zero-point term sum_d q[d] * zK[d] (one number per head and page).
-//    For G <= 8 the 16 columns hold the G heads for page A and for page B of a
-//    pair, so one B operand serves two pages.
 //  * output, transposed: O^T[d][col] += sum_slot codeV^T[d][slot] * ps[slot][col]
-//    with ps = p * sV (the per-token V scale folded into the probabilities); the
-//    32 K-slots are 4 tokens of page A and 4 of page B per lane group. For
-//    G <= 8, columns [0,G) carry the fp16 high part of ps and [G,2G) the low
-//    part; for G > 8 the two parts go through two products.
+//    with ps = p * sV (the per-token V scale folded into the probabilities);
+//    the 32 K-slots are 4 tokens of page A and 4 of page B per lane group.
+//  * column roles: for G <= 8 a column belongs to one (head, page of the pair):
+//    its logits operand carries that page's K scale and its output operand
+//    only that page's slots, so neither product needs data from another
+//    column; for G <= 4 the free columns carry the low fp16 part of the
+//    output operand. Each column keeps its own running max; the page halves
+//    (and hi / lo parts) are merged once per (sequence, head) segment. For
+//    G > 8 a column is a head and spans both pages.
 //  * fp16 hi/lo pairs keep ~22 significant bits in qs and ps, so the products
 //    add no error beyond fp32 accumulation order.
 //  * the 4-bit codes enter the matrix cores as fp16 subnormals: masking a
@@ -116,29 +119,22 @@ __device__ inline float rows_max(float v) {
   auto t = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
   return fmaxf(bitsf(t[0]), bitsf(t[1]));
 }
-// DPP controls (within rows of 16 lanes)
-constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
-constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+// DPP row rotations (within rows of 16 lanes); every lane reads a valid
+// source, so no "old" value is needed.
 constexpr int kDppRowRor4 = 0x124;    // row_ror:4  (lane c <- c-4 mod 16)
 constexpr int kDppRowRor8 = 0x128;    // row_ror:8  (lane c <- c^8)
 constexpr int kDppRowRor12 = 0x12C;   // row_ror:12 (lane c <- c+4 mod 16)
 template <int Ctrl>
 __device__ inline float dpp(float v) {
   return bitsf(static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(fbits(v)), Ctrl, 0xF, 0xF, false)));
+      __builtin_amdgcn_mov_dpp(static_cast<int>(fbits(v)), Ctrl, 0xF, 0xF, true)));
 }
-// The value of the lane holding the same head for the other page of a pair
-// (column c +- G for G <= 8). Power-of-two groups use DPP; others bpermute.
-template <int G>
-__device__ inline float pair_partner(float v, int c, int partner_lane) {
-  if constexpr (G == 1) return dpp<kDppQuadSwap1>(v);
-  else if constexpr (G == 2) return dpp<kDppQuadSwap2>(v);
-  else if constexpr (G == 4) {
-    const float up = dpp<kDppRowRor12>(v);   // from c + 4
-    const float dn = dpp<kDppRowRor4>(v);    // from c - 4
-    return (c & 4) ? dn : up;
-  } else if constexpr (G == 8) return dpp<kDppRowRor8>(v);
-  else return __shfl(v, partner_lane);
+// v of lane c ^ 8 / c ^ 4 (c = lane % 16)
+__device__ inline float xor8(float v) { return dpp<kDppRowRor8>(v); }
+__device__ inline float xor4(float v, int c) {
+  const float up = dpp<kDppRowRor12>(v);   // from c + 4
+  const float dn = dpp<kDppRowRor4>(v);    // from c - 4
+  return (c & 4) ? dn : up;
 }
 
 // qs = qc * s as an fp16 (hi, lo) pair for the 8 elements of one product,
@@ -201,43 +197,41 @@ __device__ inline void compiler_fence() { __asm__ __volatile__("" ::: "memory");
 // the DMA writes, and for compiler-visible LDS loads it would wait for every
 // outstanding DMA, draining the ring; here the caller's explicit vmcnt wait is
 // the only guard, and every output is complete when the block ends.
-struct Stage {
+struct PackedStage {
   u4 kcA, kcB, vcA, vcB;     // K / V codes of pages A and B (this lane's 16 bytes)
-  u2 svA, zvA, svB, zvB;     // V scale / zero of tokens 4g..4g+3
-  u4 sc[4], ze[4];           // K scale / zero of this lane's 32 channels, one page
+  u2 sv, zv;                 // V scale / zero of tokens 4g..4g+3 of this column's page
+  u4 sc[4], ze[4];           // K scale / zero of this lane's 32 channels, this column's page
 };
 
-// base: LDS address of the stage; page: whose K scale/zero block to read
-__device__ inline void read_stage(uint32_t base, int lane, int g, int page, Stage& r) {
+// base: LDS address of the stage; page: this column's page (0 = A, 1 = B)
+__device__ inline void read_stage_packed(uint32_t base, int lane, int g, int page, PackedStage& r) {
   const uint32_t a_lane = base + 16 * lane;
-  const uint32_t a_v = base + 8 * g;
+  const uint32_t a_v = base + 64 * page + 8 * g;
   const uint32_t a_k = base + 512 * page + 16 * g;
   __asm__ __volatile__(
-      "ds_read_b128 %0, %16\n\t"
-      "ds_read_b128 %1, %16 offset:1024\n\t"
-      "ds_read_b128 %2, %16 offset:2048\n\t"
-      "ds_read_b128 %3, %16 offset:3072\n\t"
-      "ds_read_b64 %4, %17 offset:5120\n\t"
-      "ds_read_b64 %5, %17 offset:5152\n\t"
-      "ds_read_b64 %6, %17 offset:5184\n\t"
-      "ds_read_b64 %7, %17 offset:5216\n\t"
-      "ds_read_b128 %8, %18 offset:4096\n\t"
-      "ds_read_b128 %9, %18 offset:4160\n\t"
-      "ds_read_b128 %10, %18 offset:4224\n\t"
-      "ds_read_b128 %11, %18 offset:4288\n\t"
-      "ds_read_b128 %12, %18 offset:4352\n\t"
-      "ds_read_b128 %13, %18 offset:4416\n\t"
-      "ds_read_b128 %14, %18 offset:4480\n\t"
-      "ds_read_b128 %15, %18 offset:4544\n\t"
+      "ds_read_b128 %0, %14\n\t"
+      "ds_read_b128 %1, %14 offset:1024\n\t"
+      "ds_read_b128 %2, %14 offset:2048\n\t"
+      "ds_read_b128 %3, %14 offset:3072\n\t"
+      "ds_read_b64 %4, %15 offset:5120\n\t"
+      "ds_read_b64 %5, %15 offset:5152\n\t"
+      "ds_read_b128 %6, %16 offset:4096\n\t"
+      "ds_read_b128 %7, %16 offset:4160\n\t"
+      "ds_read_b128 %8, %16 offset:4224\n\t"
+      "ds_read_b128 %9, %16 offset:4288\n\t"
+      "ds_read_b128 %10, %16 offset:4352\n\t"
+      "ds_read_b128 %11, %16 offset:4416\n\t"
+      "ds_read_b128 %12, %16 offset:4480\n\t"
+      "ds_read_b128 %13, %16 offset:4544\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.kcA), "=&v"(r.kcB), "=&v"(r.vcA), "=&v"(r.vcB), "=&v"(r.svA), "=&v"(r.zvA),
-        "=&v"(r.svB), "=&v"(r.zvB), "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]),
-        "=&v"(r.sc[3]), "=&v"(r.ze[0]), "=&v"(r.ze[1]), "=&v"(r.ze[2]), "=&v"(r.ze[3])
+      : "=&v"(r.kcA), "=&v"(r.kcB), "=&v"(r.vcA), "=&v"(r.vcB), "=&v"(r.sv), "=&v"(r.zv),
+        "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3]), "=&v"(r.ze[0]),
+        "=&v"(r.ze[1]), "=&v"(r.ze[2]), "=&v"(r.ze[3])
       : "v"(a_lane), "v"(a_v), "v"(a_k)
       : "memory");
 }
 
-// K scale / zero of one more page (wide groups read both pages)
+// K scale / zero of one page (wide groups read both pages)
 __device__ inline void read_kmeta(uint32_t base, int g, int page, u4 (&sc)[4], u4 (&ze)[4]) {
   const uint32_t a_k = base + 512 * page + 16 * g;
   __asm__ __volatile__(
@@ -254,6 +248,33 @@ __device__ inline void read_kmeta(uint32_t base, int g, int page, u4 (&sc)[4], u
         "=&v"(ze[2]), "=&v"(ze[3])
       : "v"(a_k)
       : "memory");
+}
+
+// Both pages' metadata, for groups wider than 8 (every column spans both pages).
+struct WideStage {
+  u4 kcA, kcB, vcA, vcB;
+  u2 svA, zvA, svB, zvB;
+  u4 scA[4], zeA[4], scB[4], zeB[4];
+};
+__device__ inline void read_stage_wide(uint32_t base, int lane, int g, WideStage& r) {
+  const uint32_t a_lane = base + 16 * lane;
+  const uint32_t a_v = base + 8 * g;
+  __asm__ __volatile__(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b64 %4, %9 offset:5120\n\t"
+      "ds_read_b64 %5, %9 offset:5152\n\t"
+      "ds_read_b64 %6, %9 offset:5184\n\t"
+      "ds_read_b64 %7, %9 offset:5216\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.kcA), "=&v"(r.kcB), "=&v"(r.vcA), "=&v"(r.vcB), "=&v"(r.svA), "=&v"(r.zvA),
+        "=&v"(r.svB), "=&v"(r.zvB)
+      : "v"(a_lane), "v"(a_v)
+      : "memory");
+  read_kmeta(base, g, 0, r.scA, r.zeA);
+  read_kmeta(base, g, 1, r.scB, r.zeB);
 }
 
 // units of a sequence: its full pages, plus one for a non-empty tail
@@ -305,7 +326,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ P, int32_t B, int32_t max_pages, int32_t hkv, float sm_scale,
     float* __restrict__ slots) {
-  constexpr bool kPacked = (G <= 8);  // two pages share the logits B operand
+  constexpr bool kPacked = (G <= 8);    // columns split between the two pages of a pair
+  constexpr bool kHiLoCols = (G <= 4);  // and between the hi / lo parts of the output operand
   const int w = blockIdx.x, W = gridDim.x;
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
@@ -332,13 +354,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     b0 = __builtin_amdgcn_readfirstlane(lo);
   }
 
-  // Column roles. Packed: [0,G) = (head c, page A), [G,2G) = (head c-G, page B);
-  // later columns mirror column c % G of page A so they stay finite.
-  const int head = c % G;
-  const int pslot = (kPacked && c >= G && c < 2 * G) ? 1 : 0;
-  const bool lo_col = kPacked && c >= G && c < 2 * G;
-  const int partner = kPacked ? (16 * g + ((c < G) ? c + G : (c < 2 * G ? c - G : c))) : lane;
-  auto xchg = [&](float v) -> float { return pair_partner<G>(v, c, partner); };
+  // Column roles (c = lane % 16):
+  //   G <= 4: c = 8*part + 4*page + hh  (part 0 / 1 = high / low fp16 part of
+  //           the output operand; page 0 / 1 = page A / B of a pair)
+  //   G <= 8: c = 8*page + hh
+  //   G > 8:  c = hh, both pages in every column
+  // with query head hh of the group; hh >= G are padding columns that repeat
+  // head hh % G so every value they carry stays finite.
+  const int hh = kHiLoCols ? (c & 3) : (kPacked ? (c & 7) : c);
+  const int head = hh % G;
+  const int pslot = kHiLoCols ? ((c >> 2) & 1) : (kPacked ? (c >> 3) : 0);
+  const bool lo_col = kHiLoCols && c >= 8;
   const float l2s = sm_scale * kLog2e;  // logits go to log2 units
   const float qk_scale = l2s * kQkUnscale;
   const int64_t page_stride = (int64_t)hkv * kChunkStride;
@@ -391,7 +417,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     return reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + h * G + head) * kHeadDim);
   };
   // Block ids of the pair at the producer cursor, loaded one pair ahead of
-  // their use so the scalar-load latency overlaps a whole iteration.
+  // their use so the scalar-load latency overlaps a whole iteration. A single
+  // page is fetched twice (as pages A and B) so the stage never holds stale
+  // scales.
   auto next_pair = [&](Cursor& cu) -> bool {
     while (cu.u < u1 && entry_pages(cu) == 0) advance(cu, 1);
     return cu.u < u1;
@@ -423,7 +451,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     prefetch_ids();
   };
 
-  // ---- per-(b, h) state ----
+  // ---- per-(b, h) state, per column ----
   h8 qc[4];
   float m_run = kNegInf, l_part = 0.f, lz_part = 0.f;
   f4 o[8];
@@ -455,23 +483,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   auto end_segment = [&]() {
-    if (cur_b < 0) return;
-    float l = l_part, lz = lz_part;
-    if constexpr (kPacked) {
-      // page-A and page-B lanes of a head each summed their own tokens
-      l += xchg(l);
-      lz += xchg(lz);
-    }
-    l = rows_sum(l);
-    lz = rows_sum(lz);
+    float l = rows_sum(l_part), lz = rows_sum(lz_part);
+    float m_out = m_run;
     f4 ov[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      ov[t] = o[t];
-      if constexpr (kPacked) {
+    for (int t = 0; t < 8; ++t) ov[t] = o[t];
+    if constexpr (kPacked) {
+      if constexpr (kHiLoCols) {
+        // high + low parts: same logits, same maximum, columns c and c ^ 8
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[t][i] += xchg(o[t][i]);
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[t][i] += xor8(ov[t][i]);
       }
+      // pages A and B of the pairs kept their own maxima: merge the two columns
+      auto partner = [&](float v) { return kHiLoCols ? xor4(v, c) : xor8(v); };
+      const float M = fmaxf(m_run, partner(m_run));
+      const float a = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      l *= a;
+      lz *= a;
+      l += partner(l);
+      lz += partner(lz);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = ov[t][i] * a;
+          ov[t][i] = v + partner(v);
+        }
+      m_out = M;
     }
     if (c < G) {
       const int64_t slot = (int64_t)cur_b * hkv + cur_h + w;
@@ -483,7 +523,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         for (int i = 0; i < 4; ++i) v[i] = ov[t][i] * kPvUnscale + lz;
         *reinterpret_cast<f4*>(dst + 16 * t + 4 * g) = v;
       }
-      if (g == 0) { dst[kHeadDim] = m_run; dst[kHeadDim + 1] = l; }
+      if (g == 0) { dst[kHeadDim] = m_out; dst[kHeadDim + 1] = l; }
     }
   };
 
@@ -498,8 +538,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       m_run = mnew;
     }
   };
+  // subtrahend for exp2: a column that has seen no token yet has only -inf logits
+  auto m_sub = [&]() { return (m_run == kNegInf) ? 0.f : m_run; };
 
-  // ---- fp16 tail of (cur_b, cur_h): logits and output products on fp16 values
+  // ---- fp16 tail of (cur_b, cur_h): logits and output products on fp16 values;
+  // in packed layouts only page-A columns take it
   auto process_tail = [&]() {
     const int ctx = min(ctx_lens[cur_b], max_pages * kPage);
     const int tail_n = ctx % kPage;
@@ -521,23 +564,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       const h8 qb = as_h8(ld16(qrow + 2 * (32 * m + 8 * g)));
       acc = mfma(ka, qb, acc);
     }
-    // every lane holds the tail logits of its head (all columns saw the tail)
     float lg[4];
     float mb = kNegInf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lg[i] = (4 * g + i < tail_n) ? acc[i] * l2s : kNegInf;
+      lg[i] = (4 * g + i < tail_n && pslot == 0) ? acc[i] * l2s : kNegInf;
       mb = fmaxf(mb, lg[i]);
     }
     mb = rows_max(mb);
     rescale_to(mb);
+    const float ms = m_sub();
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(lg[i] - m_run);
-    // the tail counts once per head: on page-A lanes only
-    if (pslot == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) l_part += p[i];
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(lg[i] - ms);
+      l_part += p[i];
     }
     __builtin_amdgcn_wave_barrier();
     // output: A = V tail values of tokens 4g..4g+3 (slots 0..3), slots 4..7 empty
@@ -550,7 +591,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       blo[i] = static_cast<_Float16>(x - static_cast<float>(xh));
     }
     const h8 bsel = lo_col ? blo : bhi;
-    f4 ot[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       h8 a;
@@ -559,15 +599,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         a[i] = (4 * g + i < tail_n) ? tv_s[4 * g + i][16 * t + c] : static_cast<_Float16>(0.f);
         a[4 + i] = static_cast<_Float16>(0.f);
       }
-      ot[t] = f4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kPacked) {
-        ot[t] = mfma(a, bsel, ot[t]);
+      f4 ot = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kHiLoCols) {
+        ot = mfma(a, bsel, ot);
       } else {
-        ot[t] = mfma(a, bhi, ot[t]);
-        ot[t] = mfma(a, blo, ot[t]);
+        ot = mfma(a, bhi, ot);
+        ot = mfma(a, blo, ot);
       }
       // the pages' products carry 2^-24; bring the tail's to that scale (exact)
-      o[t] += ot[t] * (1.0f / kPvUnscale);
+      o[t] += ot * (1.0f / kPvUnscale);
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -577,105 +617,128 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (const __attribute__((address_space(3))) uint8_t*)(p)));
   };
+  // fp16 (hi, lo) parts of x = p * s for output slot k (slots 2,3,6,7 carry 1/16)
+  auto ps_split = [&](float pk, _Float16 s, int k, _Float16& hi, _Float16& lo) {
+    const float sv = static_cast<float>(s) * (((k & 2) == 0) ? 1.0f : 0.0625f);
+    hi = static_cast<_Float16>(__builtin_fmaf(pk, sv, 0.0f));
+    lo = static_cast<_Float16>(__builtin_fmaf(pk, sv, -static_cast<float>(hi)));
+  };
   auto process_pair = [&](const uint8_t* st, bool has_b) {
-    Stage r;
-    read_stage(lds_addr(st), lane, g, kPacked ? pslot : 0, r);
-    const u4 kcA = r.kcA, kcB = r.kcB, vcA = r.vcA, vcB = r.vcB;
-    const u2 svA = r.svA, zvA = r.zvA, svB = r.svB, zvB = r.zvB;
-    // ---- logits ----
     f4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
-    float lgA[4], lgB[4];
-    float p_own[4], pA[4], pB[4];
     if constexpr (kPacked) {
+      PackedStage r;
+      read_stage_packed(lds_addr(st), lane, g, pslot, r);
+      // ---- logits of this column's page (K scale of that page in the operand) ----
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
         qs_split(qc[m], r.sc[m], hi, lo);
-        const h8 ka = k_operand(kcA[m]);
-        const h8 kb = k_operand(kcB[m]);
+        const h8 ka = k_operand(r.kcA[m]);
+        const h8 kb = k_operand(r.kcB[m]);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
       const float zt = rows_sum(zero_term(qc, r.ze));
-      const float zl = zt * l2s;
+      const float zl = (pslot && !has_b) ? kNegInf : zt * l2s;
       const f4 mine = pslot ? accB : accA;
-      const bool valid = !(pslot && !has_b);
-      float mb = kNegInf;
+      float lg[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lgA[k] = valid ? mine[k] * qk_scale + zl : kNegInf;
-        mb = fmaxf(mb, lgA[k]);
-      }
-      mb = rows_max(mb);
-      mb = fmaxf(mb, xchg(mb));
+      for (int k = 0; k < 4; ++k) lg[k] = mine[k] * qk_scale + zl;
+      const float mb = rows_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
       rescale_to(mb);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) p_own[k] = __builtin_amdgcn_exp2f(lgA[k] - m_run);
-      const u2 zv = pslot ? zvB : zvA;
+      const float ms = m_sub();
+      _Float16 hv[4], lv[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        l_part += p_own[k];
-        lz_part += p_own[k] * static_cast<float>(h_at2(zv, k));
-        const float other = xchg(p_own[k]);
-        pA[k] = pslot ? other : p_own[k];
-        pB[k] = pslot ? p_own[k] : other;
+        const float pk = __builtin_amdgcn_exp2f(lg[k] - ms);
+        l_part += pk;
+        lz_part += pk * static_cast<float>(h_at2(r.zv, k));
+        ps_split(pk, h_at2(r.sv, k), k, hv[k], lv[k]);
+      }
+      // this column's page occupies slots 0..3 (page A) or 4..7 (page B)
+      auto place = [&](const _Float16 (&x)[4]) -> h8 {
+        const uint32_t d0 = __builtin_bit_cast(uint32_t, h2v{x[0], x[1]});
+        const uint32_t d1 = __builtin_bit_cast(uint32_t, h2v{x[2], x[3]});
+        u4 v;
+        v[0] = pslot ? 0u : d0;
+        v[1] = pslot ? 0u : d1;
+        v[2] = pslot ? d0 : 0u;
+        v[3] = pslot ? d1 : 0u;
+        return as_h8(v);
+      };
+      if constexpr (kHiLoCols) {
+        _Float16 sel[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sel[k] = lo_col ? lv[k] : hv[k];
+        const h8 b = place(sel);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          h8 ve, vo;
+          v_operands(r.vcA[m], r.vcB[m], ve, vo);
+          o[2 * m] = mfma(ve, b, o[2 * m]);
+          o[2 * m + 1] = mfma(vo, b, o[2 * m + 1]);
+        }
+      } else {
+        const h8 bh = place(hv), bl = place(lv);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          h8 ve, vo;
+          v_operands(r.vcA[m], r.vcB[m], ve, vo);
+          o[2 * m] = mfma(ve, bh, o[2 * m]);
+          o[2 * m] = mfma(ve, bl, o[2 * m]);
+          o[2 * m + 1] = mfma(vo, bh, o[2 * m + 1]);
+          o[2 * m + 1] = mfma(vo, bl, o[2 * m + 1]);
+        }
       }
     } else {
-      u4 scB[4], zeB[4];
-      read_kmeta(lds_addr(st), g, 1, scB, zeB);
+      WideStage r;
+      read_stage_wide(lds_addr(st), lane, g, r);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
-        qs_split(qc[m], r.sc[m], hi, lo);
-        const h8 ka = k_operand(kcA[m]);
+        qs_split(qc[m], r.scA[m], hi, lo);
+        const h8 ka = k_operand(r.kcA[m]);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
-        qs_split(qc[m], scB[m], hi, lo);
-        const h8 kb = k_operand(kcB[m]);
+        qs_split(qc[m], r.scB[m], hi, lo);
+        const h8 kb = k_operand(r.kcB[m]);
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      const float zA = rows_sum(zero_term(qc, r.ze));
-      const float zB = rows_sum(zero_term(qc, zeB));
+      const float zA = rows_sum(zero_term(qc, r.zeA));
+      const float zB = rows_sum(zero_term(qc, r.zeB));
+      const float zlB = has_b ? zB * l2s : kNegInf;
+      float lgA[4], lgB[4];
       float mb = kNegInf;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         lgA[k] = accA[k] * qk_scale + zA * l2s;
-        lgB[k] = has_b ? accB[k] * qk_scale + zB * l2s : kNegInf;
+        lgB[k] = accB[k] * qk_scale + zlB;
         mb = fmaxf(mb, fmaxf(lgA[k], lgB[k]));
       }
       mb = rows_max(mb);
       rescale_to(mb);
+      h8 bhi, blo;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        pA[k] = __builtin_amdgcn_exp2f(lgA[k] - m_run);
-        pB[k] = __builtin_amdgcn_exp2f(lgB[k] - m_run);
-        l_part += pA[k] + pB[k];
-        lz_part += pA[k] * static_cast<float>(h_at2(zvA, k)) + pB[k] * static_cast<float>(h_at2(zvB, k));
+        const float pa = __builtin_amdgcn_exp2f(lgA[k] - m_run);
+        const float pb = __builtin_amdgcn_exp2f(lgB[k] - m_run);
+        l_part += pa + pb;
+        lz_part += pa * static_cast<float>(h_at2(r.zvA, k)) + pb * static_cast<float>(h_at2(r.zvB, k));
+        _Float16 h, l;
+        ps_split(pa, h_at2(r.svA, k), k, h, l);
+        bhi[k] = h;
+        blo[k] = l;
+        ps_split(pb, h_at2(r.svB, k), k + 4, h, l);
+        bhi[k + 4] = h;
+        blo[k + 4] = l;
       }
-    }
-    // ---- output product: ps = p * sV (1 or 1/16 by slot), fp16 hi/lo ----
-    h8 bhi, blo;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float pk = (k < 4) ? pA[k] : pB[k - 4];
-      const float sv = static_cast<float>(k < 4 ? h_at2(svA, k) : h_at2(svB, k - 4)) *
-                       (((k & 2) == 0) ? 1.0f : 0.0625f);
-      const _Float16 xh = static_cast<_Float16>(__builtin_fmaf(pk, sv, 0.0f));
-      bhi[k] = xh;
-      blo[k] = static_cast<_Float16>(__builtin_fmaf(pk, sv, -static_cast<float>(xh)));
-    }
-    const h8 bsel = lo_col ? blo : bhi;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      h8 ve, vo;
-      v_operands(vcA[m], vcB[m], ve, vo);
-      if constexpr (kPacked) {
-        o[2 * m] = mfma(ve, bsel, o[2 * m]);
-        o[2 * m + 1] = mfma(vo, bsel, o[2 * m + 1]);
-      } else {
+      for (int m = 0; m < 4; ++m) {
+        h8 ve, vo;
+        v_operands(r.vcA[m], r.vcB[m], ve, vo);
         o[2 * m] = mfma(ve, bhi, o[2 * m]);
         o[2 * m] = mfma(ve, blo, o[2 * m]);
         o[2 * m + 1] = mfma(vo, bhi, o[2 * m + 1]);
@@ -690,35 +753,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // (pairs issued after this one)" means this pair has landed in LDS; other
   // vector loads (query, tail) only add younger operations, which makes the
   // wait stricter, never looser.
+  auto consume_pair = [&](int np) {
+    wait_lgkmcnt0();  // the stage about to be refilled has been read out
+    compiler_fence();
+    produce();
+    const int after = issued - consumed - 1;
+    if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
+    else if (after == 1) wait_vmcnt<kDmaPerStage>();
+    else wait_vmcnt<0>();
+    compiler_fence();
+    process_pair(stage_s[consumed % kStages], np == 2);
+    compiler_fence();
+    ++consumed;
+  };
   prefetch_ids();
   produce();
   produce();
   Cursor cons = start;
   while (cons.u < u1) {
-    if (cons.b != cur_b || cons.h != cur_h) {
-      end_segment();
-      begin_segment(cons.b, cons.h);
-    }
-    const int np = entry_pages(cons);
-    if (np > 0) {
-      wait_lgkmcnt0();  // the stage about to be refilled has been read out
-      compiler_fence();
-      produce();
-      const int after = issued - consumed - 1;
-      if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
-      else if (after == 1) wait_vmcnt<kDmaPerStage>();
-      else wait_vmcnt<0>();
-      compiler_fence();
-      process_pair(stage_s[consumed % kStages], np == 2);
-      compiler_fence();
-      ++consumed;
+    begin_segment(cons.b, cons.h);
+    // the segment's pages, then its tail if the range reaches it
+    int np = entry_pages(cons);
+    while (np > 0) {
+      consume_pair(np);
       advance(cons, np);
-    } else {
+      np = (cons.u < u1 && cons.b == cur_b && cons.h == cur_h) ? entry_pages(cons) : -1;
+    }
+    if (np == 0) {
       process_tail();
       advance(cons, 1);
     }
+    end_segment();
   }
-  end_segment();
 }
 
 // Merge, for (sequence b, KV head h), the partial results of the waves whose
