@@ -9,10 +9,10 @@
 //
 // Work decomposition (persistent, balanced): the work of one launch is the flat
 // list of "units" over (sequence b, KV head h) in order, a unit being one full
-// int4 page or the fp16 tail of (b, h). decode_plan_kernel writes the prefix
-// sums of units per sequence; then a fixed grid of W one-wave work-groups (as
-// many as the GPU keeps resident) splits the list into W equal contiguous
-// ranges. Each wave streams its range through a 3-stage HBM -> LDS DMA ring,
+// int4 page or the fp16 tail of (b, h). A fixed grid of W one-wave
+// work-groups (as many as the GPU keeps resident) splits the list into W equal
+// contiguous ranges; every wave derives the per-sequence unit counts and its
+// own range from the context lengths. Each wave streams its range through a 3-stage HBM -> LDS DMA ring,
 // pairing consecutive pages of the same (b, h), and keeps an online softmax
 // (running max in log2 units, running sum, unnormalized output) for the G
 // query heads of the current (b, h); when its range crosses into the next
@@ -284,31 +284,6 @@ __device__ inline int units_of(int ctx, int max_pages) {
   return ctx / kPage + ((ctx % kPage) ? 1 : 0);
 }
 
-// P[b] = Hkv * sum_{b' < b} units(b'), P[B] = total units. One work-group.
-__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __restrict__ ctx_lens,
-                                                          int32_t B, int32_t max_pages, int32_t hkv,
-                                                          int32_t* __restrict__ P) {
-  __shared__ int32_t part[1024];
-  const int t = threadIdx.x;
-  int32_t carry = 0;
-  for (int base = 0; base < B; base += 1024) {
-    const int b = base + t;
-    const int32_t v = (b < B) ? hkv * units_of(ctx_lens[b], max_pages) : 0;
-    part[t] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int32_t x = (t >= off) ? part[t - off] : 0;
-      __syncthreads();
-      part[t] += x;
-      __syncthreads();
-    }
-    if (b < B) P[b] = carry + part[t] - v;
-    carry += part[1023];
-    __syncthreads();
-  }
-  if (t == 0) P[B] = carry;
-}
-
 // The wave that owns unit u when U units are split into W ranges
 // [w*U/W, (w+1)*U/W): the largest w with floor(w*U/W) <= u.
 __device__ __host__ inline int owner_wave(int64_t u, int64_t U, int W) {
@@ -324,7 +299,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const __half* __restrict__ q, const uint8_t* __restrict__ pages,
     const __half* __restrict__ tail_k, const __half* __restrict__ tail_v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ P, int32_t B, int32_t max_pages, int32_t hkv, float sm_scale,
+    int32_t* __restrict__ P, int32_t B, int32_t max_pages, int32_t hkv, float sm_scale,
     float* __restrict__ slots) {
   constexpr bool kPacked = (G <= 8);    // columns split between the two pages of a pair
   constexpr bool kHiLoCols = (G <= 4);  // and between the hi / lo parts of the output operand
@@ -333,26 +308,56 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int c = lane & 15, g = lane >> 4;
   const int hq = hkv * G;
 
-  const int64_t U = P[B];
+  // ---- unit plan ----
+  // units(b) = full pages of b plus one for a non-empty tail; (b, h) pairs are
+  // laid out b-major, so sequence b's units start at Hkv * sum_{b' < b} units(b').
+  // Every wave derives the total and its own start from ctx_lens; wave k % W
+  // also stores the starts of sequences 64k..64k+63 in P for the split merge.
+  int64_t U;
+  {
+    int local = 0;
+    for (int b = lane; b < B; b += 64) local += units_of(ctx_lens[b], max_pages);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
+    // every lane holds the sum; readfirstlane tells the compiler it is
+    // wave-uniform, so the range and cursor arithmetic stays scalar
+    U = (int64_t)hkv * __builtin_amdgcn_readfirstlane(local);
+  }
   const int64_t u0 = (int64_t)w * U / W;
   const int64_t u1 = (int64_t)(w + 1) * U / W;
-  if (u0 >= u1) return;
-
-  // ---- locate the sequence holding unit u0: largest b with P[b] <= u0 ----
-  int b0 = 0;
+  const bool has_range = u0 < u1;
+  const int nchunks = (B + 63) / 64;
+  int b0 = -1;
+  int64_t s0 = 0;  // first unit of sequence b0
   {
-    int lo = 0, span = B;                  // search [lo, lo + span)
-    while (span > 1) {
-      const int step = (span + 63) / 64;
-      const int idx = lo + lane * step;
-      const bool le = (idx < lo + span) && (P[idx] <= u0);
-      const uint64_t m = __ballot(le);     // lanes are in increasing idx order
-      const int last = 63 - __builtin_clzll(m);   // lane 0 always qualifies
-      lo = lo + last * step;
-      span = min(step, B - lo);
+    const int last_store = (w < nchunks) ? w + ((nchunks - 1 - w) / W) * W : -1;
+    int64_t carry = 0;
+    for (int k = 0; k < nchunks; ++k) {
+      if ((b0 >= 0 || !has_range) && k > last_store) break;
+      const int b = 64 * k + lane;
+      const int n = (b < B) ? units_of(ctx_lens[b], max_pages) : 0;
+      int incl = n;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      const int64_t start_b = (int64_t)hkv * (carry + incl - n);
+      if (k % W == w && b < B) P[b] = static_cast<int32_t>(start_b);
+      if (b0 < 0 && has_range) {
+        const uint64_t past = __ballot(b < B && start_b + (int64_t)hkv * n > u0);
+        if (past) {
+          const int lf = __builtin_ctzll(past);
+          b0 = 64 * k + lf;
+          s0 = (int64_t)hkv * (carry + __builtin_amdgcn_readfirstlane(__shfl(incl - n, lf)));
+        }
+      }
+      carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
     }
-    b0 = __builtin_amdgcn_readfirstlane(lo);
+    if (w == 0 && lane == 0) P[B] = static_cast<int32_t>(U);
   }
+  if (!has_range) return;
+  b0 = __builtin_amdgcn_readfirstlane(b0);
 
   // Column roles (c = lane % 16):
   //   G <= 4: c = 8*part + 4*page + hh  (part 0 / 1 = high / low fp16 part of
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     start.u = u0;
     start.b = b0;
     seq_info(b0, start.full, start.nunits);
-    const int64_t local = u0 - P[b0];
+    const int64_t local = u0 - s0;
     start.h = static_cast<int>(local / start.nunits);
     start.unit = static_cast<int>(local % start.nunits);
   }
@@ -788,21 +793,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 }
 
 // Merge, for (sequence b, KV head h), the partial results of the waves whose
-// unit ranges touched (b, h): an online merge over the slots, m in log2 units,
-// O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M the running max.
-// Block: 32 threads per query head of the group, 4 outputs per thread.
-__global__ __launch_bounds__(512) void splitk_reduce_kernel(
+// unit ranges touched (b, h): m in log2 units, O = sum_s 2^(m_s - M) o_s /
+// sum_s 2^(m_s - M) l_s with M the max over the slots s. The block is R slot
+// groups x (G heads x 32 output quads): each thread merges every R-th slot of
+// its quad online (independent loads, so the slot loop pipelines), then the R
+// partial merges of a quad combine through LDS.
+constexpr int kReduceThreads = 512;
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
     const float* __restrict__ slots, const int32_t* __restrict__ P,
     const int32_t* __restrict__ ctx_lens, int32_t B, int32_t max_pages, int32_t hkv, int32_t G,
     int32_t W, __half* __restrict__ out) {
+  __shared__ float red_m[kReduceThreads], red_l[kReduceThreads];
+  __shared__ f4 red_o[kReduceThreads];
   const int h = blockIdx.x, b = blockIdx.y;
-  const int jj = threadIdx.x >> 5, d0 = 4 * (threadIdx.x & 31);
+  const int C = 32 * G;
+  const int R = blockDim.x / C;
+  const int t = threadIdx.x;
+  const int combo = t % C, r = t / C;
+  const int jj = combo >> 5, d0 = 4 * (combo & 31);
   const int hq = hkv * G;
   __half* o = out + ((int64_t)b * hq + h * G + jj) * kHeadDim + d0;
   const int n = units_of(ctx_lens[b], max_pages);
   const int64_t U = P[B];
   if (n <= 0 || U <= 0) {
-    *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    if (r == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
     return;
   }
   const int64_t ustart = (int64_t)P[b] + (int64_t)h * n;
@@ -811,7 +825,8 @@ __global__ __launch_bounds__(512) void splitk_reduce_kernel(
   const int64_t bh = (int64_t)b * hkv + h;
   float M = kNegInf, L = 0.f;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int wv = wf; wv <= wl; ++wv) {
+#pragma unroll 4
+  for (int wv = wf + r; wv <= wl; wv += R) {
     // waves strictly between two owners can have empty ranges (when U < W);
     // they wrote nothing
     if ((int64_t)wv * U / W == (int64_t)(wv + 1) * U / W) continue;
@@ -825,6 +840,23 @@ __global__ __launch_bounds__(512) void splitk_reduce_kernel(
     L = L * a + ls * c;
     acc = acc * a + os * c;
     M = Mn;
+  }
+  if (R > 1) {
+    red_m[t] = M;
+    red_l[t] = L;
+    red_o[t] = acc;
+    __syncthreads();
+    if (r != 0) return;
+    for (int k = 1; k < R; ++k) {
+      const float ms = red_m[t + k * C];
+      if (ms == kNegInf) continue;
+      const float Mn = fmaxf(M, ms);
+      const float a = (M == kNegInf) ? 0.f : exp2f(M - Mn);
+      const float c = exp2f(ms - Mn);
+      L = L * a + red_l[t + k * C] * c;
+      acc = acc * a + red_o[t + k * C] * c;
+      M = Mn;
+    }
   }
   const float inv = 1.0f / L;
   __half2 lo = __floats2half2_rn(acc[0] * inv, acc[1] * inv);
@@ -854,7 +886,7 @@ size_t p_bytes(const s4kv_shape& s) { return ((size_t)(s.num_seqs + 1) * 4 + 255
 template <int G>
 hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages,
                     const void* tail_k, const void* tail_v, const int32_t* block_table,
-                    const int32_t* ctx_lens, const int32_t* P, float sm_scale, float* slots,
+                    const int32_t* ctx_lens, int32_t* P, float sm_scale, float* slots,
                     hipStream_t stream) {
   hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(W), dim3(64), 0, stream,
                      static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
@@ -880,10 +912,7 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
   float* slots = reinterpret_cast<float*>(static_cast<char*>(workspace) + p_bytes(s));
   const int W = resident_waves();
   const int G = s.num_q_heads / s.num_kv_heads;
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, ctx_lens, s.num_seqs,
-                     s.max_pages_per_seq, s.num_kv_heads, P);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   switch (G) {
 #define S4KV_CASE(g) \
   case g: e = launch_g<g>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, P, sm_scale, slots, stream); break;
@@ -894,7 +923,10 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads, s.num_seqs), dim3(32 * G), 0,
+  // slot groups per (sequence, head): as many as fit kReduceThreads
+  const int C = 32 * G;
+  const int R = (kReduceThreads / C) > 1 ? (kReduceThreads / C) : 1;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads, s.num_seqs), dim3(C * R), 0,
                      stream, slots, P, ctx_lens, s.num_seqs, s.max_pages_per_seq, s.num_kv_heads,
                      G, W, static_cast<__half*>(out));
   return hipGetLastError();
