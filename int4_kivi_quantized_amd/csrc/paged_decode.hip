@@ -171,7 +171,7 @@ __device__ inline float zero_term(const h8 (&qc)[4], const u4 (&z)[4]) {
 //   [4096,4608) K scale+zero A     [4608,5120) K scale+zero B
 //   [5120,5184) V scale+zero A     [5184,5248) V scale+zero B
 constexpr int kStageBytes = 5248;
-constexpr int kStages = 3;          // two pairs in flight while one is consumed
+constexpr int kStages = 3;          // every stage in flight while a pair is computed
 constexpr int kDmaPerStage = 6;     // DMA instructions issued per stage
 
 __device__ inline void dma16(const uint8_t* src, uint8_t* lds_base) {
@@ -416,6 +416,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // ---- DMA ring ----
   __shared__ __align__(16) uint8_t stage_s[kStages][kStageBytes];
+  __shared__ __align__(16) _Float16 tail_s[kPage][kHeadDim];  // fp16 tail V, one (b, h) at a time
   Cursor prod = start;
   int issued = 0, consumed = 0;
   auto q_row = [&](int b, int h) {
@@ -553,9 +554,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int tail_n = ctx % kPage;
     const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
     const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
-    // Stage the tail V in the ring slot the producer fills next: between two
-    // pairs at most kStages-1 pairs are in flight, so that slot is free.
-    _Float16 (*tv_s)[kHeadDim] = reinterpret_cast<_Float16 (*)[kHeadDim]>(&stage_s[issued % kStages][0]);
+    _Float16 (*tv_s)[kHeadDim] = tail_s;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -622,6 +621,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (const __attribute__((address_space(3))) uint8_t*)(p)));
   };
+  // The stage just read into registers (its asm block ended with
+  // lgkmcnt(0)) is free: refill it with the next pair at once, so three pairs
+  // are in flight while this one is computed.
+  auto refill = [&]() {
+    compiler_fence();
+    produce();
+    compiler_fence();
+  };
   // fp16 (hi, lo) parts of x = p * s for output slot k (slots 2,3,6,7 carry 1/16)
   auto ps_split = [&](float pk, _Float16 s, int k, _Float16& hi, _Float16& lo) {
     const float sv = static_cast<float>(s) * (((k & 2) == 0) ? 1.0f : 0.0625f);
@@ -633,6 +640,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if constexpr (kPacked) {
       PackedStage r;
       read_stage_packed(lds_addr(st), lane, g, pslot, r);
+      refill();
       // ---- logits of this column's page (K scale of that page in the operand) ----
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -700,6 +708,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     } else {
       WideStage r;
       read_stage_wide(lds_addr(st), lane, g, r);
+      refill();
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
@@ -753,15 +762,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   // ---- main stream ----
-  // Pairs are issued two ahead of the one consumed. vmcnt counts this wave's
-  // outstanding vector-memory operations in issue order, so "at most 6 x
-  // (pairs issued after this one)" means this pair has landed in LDS; other
-  // vector loads (query, tail) only add younger operations, which makes the
-  // wait stricter, never looser.
+  // Three pairs are issued ahead. vmcnt counts this wave's outstanding
+  // vector-memory operations in issue order, so "at most 6 x (pairs issued
+  // after this one)" means this pair has landed in LDS; other vector memory
+  // operations (query and tail loads, partial-result stores) are younger,
+  // which makes the wait stricter, never looser.
   auto consume_pair = [&](int np) {
-    wait_lgkmcnt0();  // the stage about to be refilled has been read out
-    compiler_fence();
-    produce();
     const int after = issued - consumed - 1;
     if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
     else if (after == 1) wait_vmcnt<kDmaPerStage>();
@@ -772,6 +778,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     ++consumed;
   };
   prefetch_ids();
+  produce();
   produce();
   produce();
   Cursor cons = start;
