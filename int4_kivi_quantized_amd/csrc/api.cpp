@@ -90,7 +90,7 @@ s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void
     return S4KV_ERR_INVALID_ARG;
   if (workspace_bytes < s4kv::workspace_bytes(*shape)) return S4KV_ERR_WORKSPACE;
   const hipError_t e = s4kv::launch_paged_decode(*shape, q, pages, tail_k, tail_v,
-                                                 block_table, ctx_lens, sm_scale, out, workspace,
+                                                 block_table, ctx_lens, max_ctx, sm_scale, out, workspace,
                                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
 }

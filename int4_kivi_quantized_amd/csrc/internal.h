@@ -22,7 +22,8 @@ constexpr int kOffKZero = 2304;
 constexpr int kOffVScale = 2560;
 constexpr int kOffVZero = 2592;
 
-// Decode workspace: unit prefix sums and the per-(sequence, head, wave) partials.
+// Decode workspace: the total unit count, the waves sharing each (sequence, head)
+// and the per-(sequence, head, wave) partial results.
 size_t workspace_bytes(const s4kv_shape& s);
 
 hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void* v,
@@ -33,6 +34,7 @@ hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void
 hipError_t launch_paged_decode(const s4kv_shape& s, const void* q,
                                const void* pages, const void* tail_k, const void* tail_v,
                                const int32_t* block_table, const int32_t* ctx_lens,
-                               float sm_scale, void* out, void* workspace, hipStream_t stream);
+                               int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                               hipStream_t stream);
 
 }  // namespace s4kv

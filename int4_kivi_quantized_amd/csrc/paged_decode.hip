@@ -299,8 +299,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const __half* __restrict__ q, const uint8_t* __restrict__ pages,
     const __half* __restrict__ tail_k, const __half* __restrict__ tail_v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
-    int32_t* __restrict__ P, int32_t B, int32_t max_pages, int32_t hkv, float sm_scale,
-    float* __restrict__ slots) {
+    int32_t* __restrict__ total_units, int2* __restrict__ seg_waves, int32_t B, int32_t max_pages,
+    int32_t hkv, float sm_scale, float* __restrict__ slots) {
   constexpr bool kPacked = (G <= 8);    // columns split between the two pages of a pair
   constexpr bool kHiLoCols = (G <= 4);  // and between the hi / lo parts of the output operand
   const int w = blockIdx.x, W = gridDim.x;
@@ -311,8 +311,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // ---- unit plan ----
   // units(b) = full pages of b plus one for a non-empty tail; (b, h) pairs are
   // laid out b-major, so sequence b's units start at Hkv * sum_{b' < b} units(b').
-  // Every wave derives the total and its own start from ctx_lens; wave k % W
-  // also stores the starts of sequences 64k..64k+63 in P for the split merge.
+  // Every wave derives the total and its own start from ctx_lens. The wave
+  // that owns the first unit of a (b, h) records which waves share it.
   int64_t U;
   {
     int local = 0;
@@ -326,14 +326,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int64_t u0 = (int64_t)w * U / W;
   const int64_t u1 = (int64_t)(w + 1) * U / W;
   const bool has_range = u0 < u1;
+  if (w == 0 && lane == 0) total_units[0] = static_cast<int32_t>(U);
+  if (!has_range) return;
   const int nchunks = (B + 63) / 64;
   int b0 = -1;
   int64_t s0 = 0;  // first unit of sequence b0
   {
-    const int last_store = (w < nchunks) ? w + ((nchunks - 1 - w) / W) * W : -1;
     int64_t carry = 0;
-    for (int k = 0; k < nchunks; ++k) {
-      if ((b0 >= 0 || !has_range) && k > last_store) break;
+    for (int k = 0; k < nchunks && b0 < 0; ++k) {
       const int b = 64 * k + lane;
       const int n = (b < B) ? units_of(ctx_lens[b], max_pages) : 0;
       int incl = n;
@@ -343,20 +343,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         if (lane >= off) incl += t;
       }
       const int64_t start_b = (int64_t)hkv * (carry + incl - n);
-      if (k % W == w && b < B) P[b] = static_cast<int32_t>(start_b);
-      if (b0 < 0 && has_range) {
-        const uint64_t past = __ballot(b < B && start_b + (int64_t)hkv * n > u0);
-        if (past) {
-          const int lf = __builtin_ctzll(past);
-          b0 = 64 * k + lf;
-          s0 = (int64_t)hkv * (carry + __builtin_amdgcn_readfirstlane(__shfl(incl - n, lf)));
-        }
+      const uint64_t past = __ballot(b < B && start_b + (int64_t)hkv * n > u0);
+      if (past) {
+        const int lf = __builtin_ctzll(past);
+        b0 = 64 * k + lf;
+        s0 = (int64_t)hkv * (carry + __builtin_amdgcn_readfirstlane(__shfl(incl - n, lf)));
       }
       carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
     }
-    if (w == 0 && lane == 0) P[B] = static_cast<int32_t>(U);
   }
-  if (!has_range) return;
   b0 = __builtin_amdgcn_readfirstlane(b0);
 
   // Column roles (c = lane % 16):
@@ -463,9 +458,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   f4 o[8];
   int cur_b = -1, cur_h = 0;
 
-  auto begin_segment = [&](int b, int h) {
+  auto begin_segment = [&](const Cursor& cu) {
+    const int b = cu.b, h = cu.h;
     cur_b = b;
     cur_h = h;
+    // the owner of the segment's first unit records the waves sharing it
+    const int64_t first = cu.u - cu.unit;
+    if (first >= u0 && lane == 0)
+      seg_waves[(int64_t)b * hkv + h] = make_int2(owner_wave(first, U, W), owner_wave(first + cu.nunits - 1, U, W));
     // the query of the new (b, h); loading it waits for the ring's DMAs,
     // once per segment
     u4 raw[4];
@@ -783,7 +783,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   produce();
   Cursor cons = start;
   while (cons.u < u1) {
-    begin_segment(cons.b, cons.h);
+    begin_segment(cons);
     // the segment's pages, then its tail if the range reaches it
     int np = entry_pages(cons);
     while (np > 0) {
@@ -800,16 +800,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 }
 
 // Merge, for (sequence b, KV head h), the partial results of the waves whose
-// unit ranges touched (b, h): m in log2 units, O = sum_s 2^(m_s - M) o_s /
-// sum_s 2^(m_s - M) l_s with M the max over the slots s. The block is R slot
-// groups x (G heads x 32 output quads): each thread merges every R-th slot of
-// its quad online (independent loads, so the slot loop pipelines), then the R
+// unit ranges touched (b, h) (recorded by the wave owning its first unit): m in
+// log2 units, O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M the
+// max over the slots s. The block is R slot groups x (G heads x 32 output
+// quads): each thread merges every R-th slot of its quad online, then the R
 // partial merges of a quad combine through LDS.
-constexpr int kReduceThreads = 512;
+constexpr int kReduceThreads = 1024;
 __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
-    const float* __restrict__ slots, const int32_t* __restrict__ P,
-    const int32_t* __restrict__ ctx_lens, int32_t B, int32_t max_pages, int32_t hkv, int32_t G,
-    int32_t W, __half* __restrict__ out) {
+    const float* __restrict__ slots, const int32_t* __restrict__ total_units,
+    const int2* __restrict__ seg_waves, const int32_t* __restrict__ ctx_lens, int32_t max_pages,
+    int32_t hkv, int32_t G, int32_t W, __half* __restrict__ out) {
   __shared__ float red_m[kReduceThreads], red_l[kReduceThreads];
   __shared__ f4 red_o[kReduceThreads];
   const int h = blockIdx.x, b = blockIdx.y;
@@ -820,20 +820,18 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   const int jj = combo >> 5, d0 = 4 * (combo & 31);
   const int hq = hkv * G;
   __half* o = out + ((int64_t)b * hq + h * G + jj) * kHeadDim + d0;
+  const int64_t bh = (int64_t)b * hkv + h;
   const int n = units_of(ctx_lens[b], max_pages);
-  const int64_t U = P[B];
+  const int64_t U = total_units[0];
+  const int2 ws = seg_waves[bh];
   if (n <= 0 || U <= 0) {
     if (r == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
     return;
   }
-  const int64_t ustart = (int64_t)P[b] + (int64_t)h * n;
-  const int wf = owner_wave(ustart, U, W);
-  const int wl = owner_wave(ustart + n - 1, U, W);
-  const int64_t bh = (int64_t)b * hkv + h;
   float M = kNegInf, L = 0.f;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int wv = wf + r; wv <= wl; wv += R) {
+  for (int wv = ws.x + r; wv <= ws.y; wv += R) {
     // waves strictly between two owners can have empty ranges (when U < W);
     // they wrote nothing
     if ((int64_t)wv * U / W == (int64_t)(wv + 1) * U / W) continue;
@@ -888,18 +886,23 @@ int resident_waves() {
   return cached;
 }
 
-size_t p_bytes(const s4kv_shape& s) { return ((size_t)(s.num_seqs + 1) * 4 + 255) & ~size_t(255); }
+// Workspace: [total units, padded to 256 B] [first / last wave per (b, h),
+// padded to 256 B] [partial slots].
+constexpr size_t kHeaderBytes = 256;
+size_t seg_bytes(const s4kv_shape& s) {
+  return ((size_t)s.num_seqs * s.num_kv_heads * sizeof(int2) + 255) & ~size_t(255);
+}
 
 template <int G>
 hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages,
                     const void* tail_k, const void* tail_v, const int32_t* block_table,
-                    const int32_t* ctx_lens, int32_t* P, float sm_scale, float* slots,
-                    hipStream_t stream) {
+                    const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves, float sm_scale,
+                    float* slots, hipStream_t stream) {
   hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(W), dim3(64), 0, stream,
                      static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
                      static_cast<const __half*>(tail_k), static_cast<const __half*>(tail_v),
-                     block_table, ctx_lens, P, s.num_seqs, s.max_pages_per_seq, s.num_kv_heads,
-                     sm_scale, slots);
+                     block_table, ctx_lens, total_units, seg_waves, s.num_seqs, s.max_pages_per_seq,
+                     s.num_kv_heads, sm_scale, slots);
   return hipGetLastError();
 }
 
@@ -908,21 +911,24 @@ hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages
 size_t workspace_bytes(const s4kv_shape& s) {
   const size_t nslots = (size_t)s.num_seqs * s.num_kv_heads + kMaxWaves;
   const int G = s.num_q_heads / s.num_kv_heads;
-  return p_bytes(s) + nslots * G * kSlotStride * sizeof(float);
+  return kHeaderBytes + seg_bytes(s) + nslots * G * kSlotStride * sizeof(float);
 }
 
 hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* pages,
                                const void* tail_k, const void* tail_v,
                                const int32_t* block_table, const int32_t* ctx_lens,
-                               float sm_scale, void* out, void* workspace, hipStream_t stream) {
-  int32_t* P = static_cast<int32_t*>(workspace);
-  float* slots = reinterpret_cast<float*>(static_cast<char*>(workspace) + p_bytes(s));
+                               int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                               hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int32_t* total_units = reinterpret_cast<int32_t*>(ws);
+  int2* seg_waves = reinterpret_cast<int2*>(ws + kHeaderBytes);
+  float* slots = reinterpret_cast<float*>(ws + kHeaderBytes + seg_bytes(s));
   const int W = resident_waves();
   const int G = s.num_q_heads / s.num_kv_heads;
   hipError_t e = hipSuccess;
   switch (G) {
 #define S4KV_CASE(g) \
-  case g: e = launch_g<g>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, P, sm_scale, slots, stream); break;
+  case g: e = launch_g<g>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, total_units, seg_waves, sm_scale, slots, stream); break;
     S4KV_CASE(1) S4KV_CASE(2) S4KV_CASE(3) S4KV_CASE(4) S4KV_CASE(5) S4KV_CASE(6) S4KV_CASE(7)
     S4KV_CASE(8) S4KV_CASE(9) S4KV_CASE(10) S4KV_CASE(11) S4KV_CASE(12) S4KV_CASE(13)
     S4KV_CASE(14) S4KV_CASE(15) S4KV_CASE(16)
@@ -930,12 +936,19 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  // slot groups per (sequence, head): as many as fit kReduceThreads
+  // Slot groups per (sequence, head): about the number of waves that share a
+  // (b, h) when every context is max_ctx long (W waves over B * Hkv * pages
+  // units), rounded up to a power of two and capped by the block size. This
+  // only sizes the launch; any count of sharing waves is merged correctly.
   const int C = 32 * G;
-  const int R = (kReduceThreads / C) > 1 ? (kReduceThreads / C) : 1;
+  const int64_t per_bh = ((int64_t)max_ctx + kPage - 1) / kPage;
+  const int64_t units = (int64_t)s.num_seqs * s.num_kv_heads * per_bh;
+  const int64_t share = (int64_t)W * per_bh / (units > 0 ? units : 1) + 2;
+  int R = 1;
+  while (R < share && 2 * R * C <= kReduceThreads) R *= 2;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads, s.num_seqs), dim3(C * R), 0,
-                     stream, slots, P, ctx_lens, s.num_seqs, s.max_pages_per_seq, s.num_kv_heads,
-                     G, W, static_cast<__half*>(out));
+                     stream, slots, total_units, seg_waves, ctx_lens, s.max_pages_per_seq,
+                     s.num_kv_heads, G, W, static_cast<__half*>(out));
   return hipGetLastError();
 }
 
