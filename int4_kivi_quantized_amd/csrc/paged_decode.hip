@@ -149,19 +149,21 @@ __device__ inline void qs_split(h8 qc, u4 s, h8& hi, h8& lo) {
 
 __device__ inline h2v half_pair(h8 v, int k) { return h2v{v[2 * k], v[2 * k + 1]}; }
 
-// sum_d q[d] * z[d] over this lane's 32 channels (dot2 on fp16 pairs); qc
-// carries 2^-4 on slots 0,1,4,5 and 2^-8 on slots 2,3,6,7.
-__device__ inline float zero_term(const h8 (&qc)[4], const u4 (&z)[4]) {
-  float a = 0.f, b = 0.f;
+// Zero-point term of the logits, sum_d q[d] * zK[d], for both pages of a
+// pair on the matrix cores: with every row of A equal to one page's K zeros
+// (each lane supplies its 8 channels of product m) and B the plain query of
+// the lane's head, every row of D holds that page's term for each column.
+// fp16 x fp16 products are exact in the fp32 accumulation.
+__device__ inline void zero_terms(const h8 (&qh)[4], const u4 (&za)[4], const u4 (&zb)[4],
+                                  float& ta, float& tb) {
+  f4 da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const h8 zz = as_h8(z[m]);
-    a = __builtin_amdgcn_fdot2(half_pair(qc[m], 0), half_pair(zz, 0), a, false);
-    b = __builtin_amdgcn_fdot2(half_pair(qc[m], 1), half_pair(zz, 1), b, false);
-    a = __builtin_amdgcn_fdot2(half_pair(qc[m], 2), half_pair(zz, 2), a, false);
-    b = __builtin_amdgcn_fdot2(half_pair(qc[m], 3), half_pair(zz, 3), b, false);
+    da = mfma(as_h8(za[m]), qh[m], da);
+    db = mfma(as_h8(zb[m]), qh[m], db);
   }
-  return 16.f * a + 256.f * b;
+  ta = da[0];
+  tb = db[0];
 }
 
 // A stage holds one pair of pages, copied HBM -> LDS by the DMA path
@@ -200,7 +202,8 @@ __device__ inline void compiler_fence() { __asm__ __volatile__("" ::: "memory");
 struct PackedStage {
   u4 kcA, kcB, vcA, vcB;     // K / V codes of pages A and B (this lane's 16 bytes)
   u2 sv, zv;                 // V scale / zero of tokens 4g..4g+3 of this column's page
-  u4 sc[4], ze[4];           // K scale / zero of this lane's 32 channels, this column's page
+  u4 sc[4];                  // K scale of this lane's 32 channels, this column's page
+  u4 zeA[4], zeB[4];         // K zero of this lane's 32 channels, pages A and B
 };
 
 // base: LDS address of the stage; page: this column's page (0 = A, 1 = B)
@@ -208,26 +211,32 @@ __device__ inline void read_stage_packed(uint32_t base, int lane, int g, int pag
   const uint32_t a_lane = base + 16 * lane;
   const uint32_t a_v = base + 64 * page + 8 * g;
   const uint32_t a_k = base + 512 * page + 16 * g;
+  const uint32_t a_z = base + 16 * g;
   __asm__ __volatile__(
-      "ds_read_b128 %0, %14\n\t"
-      "ds_read_b128 %1, %14 offset:1024\n\t"
-      "ds_read_b128 %2, %14 offset:2048\n\t"
-      "ds_read_b128 %3, %14 offset:3072\n\t"
-      "ds_read_b64 %4, %15 offset:5120\n\t"
-      "ds_read_b64 %5, %15 offset:5152\n\t"
-      "ds_read_b128 %6, %16 offset:4096\n\t"
-      "ds_read_b128 %7, %16 offset:4160\n\t"
-      "ds_read_b128 %8, %16 offset:4224\n\t"
-      "ds_read_b128 %9, %16 offset:4288\n\t"
-      "ds_read_b128 %10, %16 offset:4352\n\t"
-      "ds_read_b128 %11, %16 offset:4416\n\t"
-      "ds_read_b128 %12, %16 offset:4480\n\t"
-      "ds_read_b128 %13, %16 offset:4544\n\t"
+      "ds_read_b128 %0, %18\n\t"
+      "ds_read_b128 %1, %18 offset:1024\n\t"
+      "ds_read_b128 %2, %18 offset:2048\n\t"
+      "ds_read_b128 %3, %18 offset:3072\n\t"
+      "ds_read_b64 %4, %19 offset:5120\n\t"
+      "ds_read_b64 %5, %19 offset:5152\n\t"
+      "ds_read_b128 %6, %20 offset:4096\n\t"
+      "ds_read_b128 %7, %20 offset:4160\n\t"
+      "ds_read_b128 %8, %20 offset:4224\n\t"
+      "ds_read_b128 %9, %20 offset:4288\n\t"
+      "ds_read_b128 %10, %21 offset:4352\n\t"
+      "ds_read_b128 %11, %21 offset:4416\n\t"
+      "ds_read_b128 %12, %21 offset:4480\n\t"
+      "ds_read_b128 %13, %21 offset:4544\n\t"
+      "ds_read_b128 %14, %21 offset:4864\n\t"
+      "ds_read_b128 %15, %21 offset:4928\n\t"
+      "ds_read_b128 %16, %21 offset:4992\n\t"
+      "ds_read_b128 %17, %21 offset:5056\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r.kcA), "=&v"(r.kcB), "=&v"(r.vcA), "=&v"(r.vcB), "=&v"(r.sv), "=&v"(r.zv),
-        "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3]), "=&v"(r.ze[0]),
-        "=&v"(r.ze[1]), "=&v"(r.ze[2]), "=&v"(r.ze[3])
-      : "v"(a_lane), "v"(a_v), "v"(a_k)
+        "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3]), "=&v"(r.zeA[0]),
+        "=&v"(r.zeA[1]), "=&v"(r.zeA[2]), "=&v"(r.zeA[3]), "=&v"(r.zeB[0]), "=&v"(r.zeB[1]),
+        "=&v"(r.zeB[2]), "=&v"(r.zeB[3])
+      : "v"(a_lane), "v"(a_v), "v"(a_k), "v"(a_z)
       : "memory");
 }
 
@@ -453,7 +462,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   // ---- per-(b, h) state, per column ----
-  h8 qc[4];
+  h8 qc[4];  // query of the column's head, pre-scaled for the code operands
+  h8 qh[4];  // the same query, plain (zero-point term)
   float m_run = kNegInf, l_part = 0.f, lz_part = 0.f;
   f4 o[8];
   int cur_b = -1, cur_h = 0;
@@ -477,6 +487,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       // element i of product m is channel 32m+8g+i, pre-scaled by 2^-4
       // (slots 0,1,4,5) or 2^-8 (slots 2,3,6,7)
       const h8 v = as_h8(raw[m]);
+      qh[m] = v;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         qc[m][i] = static_cast<_Float16>(static_cast<float>(v[i]) * (((i & 2) == 0) ? 0.0625f : 0.00390625f));
@@ -653,8 +664,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      const float zt = rows_sum(zero_term(qc, r.ze));
-      const float zl = (pslot && !has_b) ? kNegInf : zt * l2s;
+      float za, zb;
+      zero_terms(qh, r.zeA, r.zeB, za, zb);
+      const float zl = (pslot && !has_b) ? kNegInf : (pslot ? zb : za) * l2s;
       const f4 mine = pslot ? accB : accA;
       float lg[4];
 #pragma unroll
@@ -721,8 +733,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
-      const float zA = rows_sum(zero_term(qc, r.zeA));
-      const float zB = rows_sum(zero_term(qc, r.zeB));
+      float zA, zB;
+      zero_terms(qh, r.zeA, r.zeB, zA, zB);
       const float zlB = has_b ? zB * l2s : kNegInf;
       float lgA[4], lgB[4];
       float mb = kNegInf;
