@@ -307,8 +307,8 @@ def main():
         "decode_tokens_per_s": round(r["tokens_per_s"], 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "one s4kv_paged_decode call on one layer (its three launches: unit plan, "
-                      "decode stream, split merge), timed with HIP events on the call's stream",
+            "kernel": "one s4kv_paged_decode call on one layer (its two launches: decode stream, "
+                      "split merge), timed with HIP events on the call's stream",
             "achieved": round(r["decode_launch_gbs"], 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
