@@ -15,8 +15,8 @@
 // own range from the context lengths. Each wave streams its range through a 3-stage HBM -> LDS DMA ring,
 // pairing consecutive pages of the same (b, h), and keeps an online softmax
 // (running max in log2 units, running sum, unnormalized output) for the G
-// query heads of the current (b, h); when its range crosses into the next
-// (b, h) it writes the partial result to workspace slot (b*Hkv + h) + wave.
+// query heads of the current (b, h); each (b, h) its range touches yields a
+// partial result in workspace slot (b*Hkv + h) + wave.
 // splitk_reduce_kernel merges, for each (b, query head), the partials of the
 // consecutive waves whose ranges touched it.
 //
@@ -149,21 +149,22 @@ __device__ inline void qs_split(h8 qc, u4 s, h8& hi, h8& lo) {
 
 __device__ inline h2v half_pair(h8 v, int k) { return h2v{v[2 * k], v[2 * k + 1]}; }
 
-// Zero-point term of the logits, sum_d q[d] * zK[d], for both pages of a
-// pair on the matrix cores: with every row of A equal to one page's K zeros
-// (each lane supplies its 8 channels of product m) and B the plain query of
-// the lane's head, every row of D holds that page's term for each column.
-// fp16 x fp16 products are exact in the fp32 accumulation.
-__device__ inline void zero_terms(const h8 (&qh)[4], const u4 (&za)[4], const u4 (&zb)[4],
-                                  float& ta, float& tb) {
-  f4 da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+// Zero-point terms of the logits, sum_d q[d] * zK[d], for both pages of a
+// pair in one chain of products: rows 0..7 of A are page A's K zeros and rows
+// 8..15 page B's (lane (c, g) supplies row c, its 8 channels of product m), B
+// is the plain query of the lane's head. D rows 4g..4g+3 sit in the lanes of
+// group g, so lanes 0..31 hold page A's term for their column and lanes
+// 32..63 page B's; swapping the two halves gives every lane both. fp16 x fp16
+// products are exact in the fp32 accumulation.
+__device__ inline void zero_terms(const h8 (&qh)[4], const u4 (&z)[4], float& ta, float& tb) {
+  f4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    da = mfma(as_h8(za[m]), qh[m], da);
-    db = mfma(as_h8(zb[m]), qh[m], db);
-  }
-  ta = da[0];
-  tb = db[0];
+  for (int m = 0; m < 4; ++m) d = mfma(as_h8(z[m]), qh[m], d);
+  // permlane32_swap(x, x): first result = x of lane l % 32 (lower half),
+  // second = x of lane 32 + l % 32 (upper half)
+  const auto r = __builtin_amdgcn_permlane32_swap(fbits(d[0]), fbits(d[0]), false, false);
+  ta = bitsf(r[0]);
+  tb = bitsf(r[1]);
 }
 
 // A stage holds one pair of pages, copied HBM -> LDS by the DMA path
@@ -203,59 +204,51 @@ struct PackedStage {
   u4 kcA, kcB, vcA, vcB;     // K / V codes of pages A and B (this lane's 16 bytes)
   u2 sv, zv;                 // V scale / zero of tokens 4g..4g+3 of this column's page
   u4 sc[4];                  // K scale of this lane's 32 channels, this column's page
-  u4 zeA[4], zeB[4];         // K zero of this lane's 32 channels, pages A and B
+  u4 ze[4];                  // K zero of this lane's 32 channels, page A for rows c < 8, B above
 };
 
-// base: LDS address of the stage; page: this column's page (0 = A, 1 = B)
-__device__ inline void read_stage_packed(uint32_t base, int lane, int g, int page, PackedStage& r) {
+// base: LDS address of the stage; page: this column's page (0 = A, 1 = B);
+// zrow: page whose K zeros this lane supplies as row c of the zero-term
+// product (0 for c < 8, 1 for c >= 8)
+__device__ inline void read_stage_packed(uint32_t base, int lane, int g, int page, int zrow,
+                                         PackedStage& r) {
   const uint32_t a_lane = base + 16 * lane;
   const uint32_t a_v = base + 64 * page + 8 * g;
   const uint32_t a_k = base + 512 * page + 16 * g;
-  const uint32_t a_z = base + 16 * g;
+  const uint32_t a_z = base + 512 * zrow + 16 * g;
   __asm__ __volatile__(
-      "ds_read_b128 %0, %18\n\t"
-      "ds_read_b128 %1, %18 offset:1024\n\t"
-      "ds_read_b128 %2, %18 offset:2048\n\t"
-      "ds_read_b128 %3, %18 offset:3072\n\t"
-      "ds_read_b64 %4, %19 offset:5120\n\t"
-      "ds_read_b64 %5, %19 offset:5152\n\t"
-      "ds_read_b128 %6, %20 offset:4096\n\t"
-      "ds_read_b128 %7, %20 offset:4160\n\t"
-      "ds_read_b128 %8, %20 offset:4224\n\t"
-      "ds_read_b128 %9, %20 offset:4288\n\t"
-      "ds_read_b128 %10, %21 offset:4352\n\t"
-      "ds_read_b128 %11, %21 offset:4416\n\t"
-      "ds_read_b128 %12, %21 offset:4480\n\t"
-      "ds_read_b128 %13, %21 offset:4544\n\t"
-      "ds_read_b128 %14, %21 offset:4864\n\t"
-      "ds_read_b128 %15, %21 offset:4928\n\t"
-      "ds_read_b128 %16, %21 offset:4992\n\t"
-      "ds_read_b128 %17, %21 offset:5056\n\t"
+      "ds_read_b128 %0, %14\n\t"
+      "ds_read_b128 %1, %14 offset:1024\n\t"
+      "ds_read_b128 %2, %14 offset:2048\n\t"
+      "ds_read_b128 %3, %14 offset:3072\n\t"
+      "ds_read_b64 %4, %15 offset:5120\n\t"
+      "ds_read_b64 %5, %15 offset:5152\n\t"
+      "ds_read_b128 %6, %16 offset:4096\n\t"
+      "ds_read_b128 %7, %16 offset:4160\n\t"
+      "ds_read_b128 %8, %16 offset:4224\n\t"
+      "ds_read_b128 %9, %16 offset:4288\n\t"
+      "ds_read_b128 %10, %17 offset:4352\n\t"
+      "ds_read_b128 %11, %17 offset:4416\n\t"
+      "ds_read_b128 %12, %17 offset:4480\n\t"
+      "ds_read_b128 %13, %17 offset:4544\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r.kcA), "=&v"(r.kcB), "=&v"(r.vcA), "=&v"(r.vcB), "=&v"(r.sv), "=&v"(r.zv),
-        "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3]), "=&v"(r.zeA[0]),
-        "=&v"(r.zeA[1]), "=&v"(r.zeA[2]), "=&v"(r.zeA[3]), "=&v"(r.zeB[0]), "=&v"(r.zeB[1]),
-        "=&v"(r.zeB[2]), "=&v"(r.zeB[3])
+        "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3]), "=&v"(r.ze[0]),
+        "=&v"(r.ze[1]), "=&v"(r.ze[2]), "=&v"(r.ze[3])
       : "v"(a_lane), "v"(a_v), "v"(a_k), "v"(a_z)
       : "memory");
 }
 
-// K scale / zero of one page (wide groups read both pages)
-__device__ inline void read_kmeta(uint32_t base, int g, int page, u4 (&sc)[4], u4 (&ze)[4]) {
-  const uint32_t a_k = base + 512 * page + 16 * g;
+// K scale of one page, or (at byte offset 256 past it) K zero
+__device__ inline void read_kvec(uint32_t addr, u4 (&v)[4]) {
   __asm__ __volatile__(
-      "ds_read_b128 %0, %8 offset:4096\n\t"
-      "ds_read_b128 %1, %8 offset:4160\n\t"
-      "ds_read_b128 %2, %8 offset:4224\n\t"
-      "ds_read_b128 %3, %8 offset:4288\n\t"
-      "ds_read_b128 %4, %8 offset:4352\n\t"
-      "ds_read_b128 %5, %8 offset:4416\n\t"
-      "ds_read_b128 %6, %8 offset:4480\n\t"
-      "ds_read_b128 %7, %8 offset:4544\n\t"
+      "ds_read_b128 %0, %4 offset:4096\n\t"
+      "ds_read_b128 %1, %4 offset:4160\n\t"
+      "ds_read_b128 %2, %4 offset:4224\n\t"
+      "ds_read_b128 %3, %4 offset:4288\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3]), "=&v"(ze[0]), "=&v"(ze[1]),
-        "=&v"(ze[2]), "=&v"(ze[3])
-      : "v"(a_k)
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(addr)
       : "memory");
 }
 
@@ -263,9 +256,9 @@ __device__ inline void read_kmeta(uint32_t base, int g, int page, u4 (&sc)[4], u
 struct WideStage {
   u4 kcA, kcB, vcA, vcB;
   u2 svA, zvA, svB, zvB;
-  u4 scA[4], zeA[4], scB[4], zeB[4];
+  u4 scA[4], scB[4], ze[4];
 };
-__device__ inline void read_stage_wide(uint32_t base, int lane, int g, WideStage& r) {
+__device__ inline void read_stage_wide(uint32_t base, int lane, int g, int zrow, WideStage& r) {
   const uint32_t a_lane = base + 16 * lane;
   const uint32_t a_v = base + 8 * g;
   __asm__ __volatile__(
@@ -282,8 +275,9 @@ __device__ inline void read_stage_wide(uint32_t base, int lane, int g, WideStage
         "=&v"(r.svB), "=&v"(r.zvB)
       : "v"(a_lane), "v"(a_v)
       : "memory");
-  read_kmeta(base, g, 0, r.scA, r.zeA);
-  read_kmeta(base, g, 1, r.scB, r.zeB);
+  read_kvec(base + 16 * g, r.scA);
+  read_kvec(base + 512 + 16 * g, r.scB);
+  read_kvec(base + 512 * zrow + 256 + 16 * g, r.ze);
 }
 
 // units of a sequence: its full pages, plus one for a non-empty tail
@@ -374,6 +368,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int head = hh % G;
   const int pslot = kHiLoCols ? ((c >> 2) & 1) : (kPacked ? (c >> 3) : 0);
   const bool lo_col = kHiLoCols && c >= 8;
+  const int zrow = c >> 3;  // page of the K zeros this lane supplies (zero-term product)
   const float l2s = sm_scale * kLog2e;  // logits go to log2 units
   const float qk_scale = l2s * kQkUnscale;
   const int64_t page_stride = (int64_t)hkv * kChunkStride;
@@ -499,12 +494,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int t = 0; t < 8; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
   };
 
+  // Partial-result stores wait for nothing, but while they are outstanding
+  // they hold vmcnt, so the ring's next waits would stall on them (their
+  // write-back is slow under a full read stream). A packed layout therefore
+  // keeps a finished segment's partial in registers and writes it when the
+  // next segment ends, or when the range is done -- for most waves, after the
+  // last ring wait. After the page merge every head's values sit in
+  // kCopies columns, so each copy keeps a different 1/kCopies of the outputs.
+  constexpr int kCopies = kHiLoCols ? 4 : 2;  // columns holding the same head
+  constexpr int kKeep = 8 / kCopies;          // output tiles kept per lane
+  const int copy = kHiLoCols ? (c >> 2) : (c >> 3);
+  const int head_col = kHiLoCols ? (c & 3) : (c & 7);
+  f4 keep_o[kKeep];
+  float keep_m = 0.f, keep_l = 0.f;
+  int64_t keep_slot = -1;  // wave-uniform; -1 when nothing is held
+  auto store_kept = [&]() {
+    if (keep_slot < 0) return;
+    if (head_col < G) {
+      float* dst = slots + (keep_slot * G + head_col) * kSlotStride;
+#pragma unroll
+      for (int n = 0; n < kKeep; ++n)
+        *reinterpret_cast<f4*>(dst + 16 * (kKeep * copy + n) + 4 * g) = keep_o[n];
+      if (g == 0 && copy == 0) { dst[kHeadDim] = keep_m; dst[kHeadDim + 1] = keep_l; }
+    }
+    keep_slot = -1;
+  };
+
   auto end_segment = [&]() {
     float l = rows_sum(l_part), lz = rows_sum(lz_part);
     float m_out = m_run;
     f4 ov[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) ov[t] = o[t];
+    const int64_t slot = (int64_t)cur_b * hkv + cur_h + w;
     if constexpr (kPacked) {
       if constexpr (kHiLoCols) {
         // high + low parts: same logits, same maximum, columns c and c ^ 8
@@ -529,18 +551,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           ov[t][i] = v + partner(v);
         }
       m_out = M;
-    }
-    if (c < G) {
-      const int64_t slot = (int64_t)cur_b * hkv + cur_h + w;
-      float* dst = slots + (slot * G + c) * kSlotStride;
+      // write the partial held from an earlier segment, hold this one
+      store_kept();
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        f4 v;
+      for (int n = 0; n < kKeep; ++n) {
+        f4 v = ov[n];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = ov[t][i] * kPvUnscale + lz;
-        *reinterpret_cast<f4*>(dst + 16 * t + 4 * g) = v;
+        for (int k = 1; k < kCopies; ++k)
+          if (copy == k) v = ov[kKeep * k + n];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) keep_o[n][i] = v[i] * kPvUnscale + lz;
       }
-      if (g == 0) { dst[kHeadDim] = m_out; dst[kHeadDim + 1] = l; }
+      keep_m = m_out;
+      keep_l = l;
+      keep_slot = slot;
+    } else {
+      if (c < G) {
+        float* dst = slots + (slot * G + c) * kSlotStride;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          f4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = ov[t][i] * kPvUnscale + lz;
+          *reinterpret_cast<f4*>(dst + 16 * t + 4 * g) = v;
+        }
+        if (g == 0) { dst[kHeadDim] = m_out; dst[kHeadDim + 1] = l; }
+      }
     }
   };
 
@@ -650,7 +686,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     f4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kPacked) {
       PackedStage r;
-      read_stage_packed(lds_addr(st), lane, g, pslot, r);
+      read_stage_packed(lds_addr(st), lane, g, pslot, zrow, r);
       refill();
       // ---- logits of this column's page (K scale of that page in the operand) ----
 #pragma unroll
@@ -665,7 +701,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         accB = mfma(kb, lo, accB);
       }
       float za, zb;
-      zero_terms(qh, r.zeA, r.zeB, za, zb);
+      zero_terms(qh, r.ze, za, zb);
       const float zl = (pslot && !has_b) ? kNegInf : (pslot ? zb : za) * l2s;
       const f4 mine = pslot ? accB : accA;
       float lg[4];
@@ -719,7 +755,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     } else {
       WideStage r;
-      read_stage_wide(lds_addr(st), lane, g, r);
+      read_stage_wide(lds_addr(st), lane, g, zrow, r);
       refill();
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -734,7 +770,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         accB = mfma(kb, lo, accB);
       }
       float zA, zB;
-      zero_terms(qh, r.zeA, r.zeB, zA, zB);
+      zero_terms(qh, r.ze, zA, zB);
       const float zlB = has_b ? zB * l2s : kNegInf;
       float lgA[4], lgB[4];
       float mb = kNegInf;
@@ -809,6 +845,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
     end_segment();
   }
+  if constexpr (kPacked) store_kept();
 }
 
 // Merge, for (sequence b, KV head h), the partial results of the waves whose
