@@ -65,6 +65,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kQkUnscale = 268435456.0f;  // 2^28
 constexpr float kPvUnscale = 16777216.0f;   // 2^24
 constexpr int kMaxWaves = 4096;             // upper bound on the persistent grid
+// A V scale is at most (65504 + 65504) / 15 < 2^13.1 and fp16 holds values
+// below 2^16, so p * sV stays finite while p <= 2^2.
+constexpr float kLazyRescale = 2.0f;
 
 __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 
@@ -380,17 +383,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     int unit;    // unit inside (b, h)
     int full;    // full pages of b
     int nunits;  // units of b
+    int tail;    // tokens in the fp16 tail of b
   };
-  auto seq_info = [&](int b, int& full, int& nunits) {
+  auto seq_info = [&](int b, Cursor& cu) {
     const int ctx = min(ctx_lens[b], max_pages * kPage);
-    full = ctx > 0 ? ctx / kPage : 0;
-    nunits = units_of(ctx, max_pages);
+    cu.full = ctx > 0 ? ctx / kPage : 0;
+    cu.tail = ctx > 0 ? ctx % kPage : 0;
+    cu.nunits = cu.full + (cu.tail ? 1 : 0);
   };
   Cursor start;
   {
     start.u = u0;
     start.b = b0;
-    seq_info(b0, start.full, start.nunits);
+    seq_info(b0, start);
     const int64_t local = u0 - s0;
     start.h = static_cast<int>(local / start.nunits);
     start.unit = static_cast<int>(local % start.nunits);
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       cu.unit = 0;
       if (++cu.h == hkv) {
         cu.h = 0;
-        do { ++cu.b; seq_info(cu.b, cu.full, cu.nunits); } while (cu.nunits == 0);
+        do { ++cu.b; seq_info(cu.b, cu); } while (cu.nunits == 0);
       }
     }
   };
@@ -580,9 +585,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
   };
 
+  // The reference max of a column moves only when a logit passes it by more
+  // than kLazyRescale (log2 units), so most pages skip rescaling the
+  // accumulators; a probability is then at most 2^kLazyRescale, which keeps
+  // p * sV inside the fp16 range for every fp16 V scale.
   auto rescale_to = [&](float mb) {
-    const float mnew = fmaxf(m_run, mb);
-    if (__any(mnew > m_run)) {
+    const bool up = mb > m_run + kLazyRescale;
+    if (__any(up)) {
+      const float mnew = up ? mb : m_run;
       const float alpha = (mnew == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
       l_part *= alpha;
       lz_part *= alpha;
@@ -596,9 +606,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // ---- fp16 tail of (cur_b, cur_h): logits and output products on fp16 values;
   // in packed layouts only page-A columns take it
-  auto process_tail = [&]() {
-    const int ctx = min(ctx_lens[cur_b], max_pages * kPage);
-    const int tail_n = ctx % kPage;
+  auto process_tail = [&](int tail_n) {
     const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
     const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
     _Float16 (*tv_s)[kHeadDim] = tail_s;
@@ -607,14 +615,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int i = 0; i < 4; ++i)
       reinterpret_cast<u4*>(&tv_s[0][0])[lane + 64 * i] = ld16(tv + 16 * (lane + 64 * i));
     // logits: A = K tail values (token c, channels 32m+8g..+8), B = plain q
-    const uint8_t* qrow = q_row(cur_b, cur_h);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const h8 ka = as_h8(ld16(tk + 2 * (c * kHeadDim + 32 * m + 8 * g)));
-      const h8 qb = as_h8(ld16(qrow + 2 * (32 * m + 8 * g)));
-      acc = mfma(ka, qb, acc);
-    }
+    for (int m = 0; m < 4; ++m) acc = mfma(as_h8(ld16(tk + 2 * (c * kHeadDim + 32 * m + 8 * g))), qh[m], acc);
     float lg[4];
     float mb = kNegInf;
 #pragma unroll
@@ -811,10 +814,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // ---- main stream ----
   // Three pairs are issued ahead. vmcnt counts this wave's outstanding
-  // vector-memory operations in issue order, so "at most 6 x (pairs issued
-  // after this one)" means this pair has landed in LDS; other vector memory
-  // operations (query and tail loads, partial-result stores) are younger,
-  // which makes the wait stricter, never looser.
+  // vector-memory operations and loads complete in issue order, so "at most
+  // 6 x (pairs issued after this one)" outstanding means this pair has landed
+  // in LDS; other outstanding operations (query and tail loads,
+  // partial-result stores) can only make the wait stricter.
   auto consume_pair = [&](int np) {
     const int after = issued - consumed - 1;
     if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
@@ -840,7 +843,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       np = (cons.u < u1 && cons.b == cur_b && cons.h == cur_h) ? entry_pages(cons) : -1;
     }
     if (np == 0) {
-      process_tail();
+      process_tail(cons.tail);
       advance(cons, 1);
     }
     end_segment();
