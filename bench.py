@@ -10,7 +10,8 @@ Headline workload: Llama-3.1-8B-shaped decode, 32 layers, 32 query / 8 KV
 heads, head_dim 128, batch 128, contexts U[2048, 8192], page 16.
 Secondary (same JSON line): Llama-3-70B-shaped decode, 80 layers, 64/8 heads,
 batch 16, 32768-token contexts, with the bulk prefill quantize of those
-contexts timed separately.
+contexts timed separately; and the fp16 control path (the same decode over an
+fp16 paged cache) against the int4 call on one layer of the headline workload.
 
 Prints one JSON line. `value` is KV GB/s: the algorithmic bytes of all decode
 launches of a step (pages, tails, block-table entries, Q, O) divided by the
@@ -235,6 +236,72 @@ def copy_ceiling(nbytes=1 << 30, reps=10):
             "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 2)}
 
 
+def fp16_control(wl, calls=20, warmup=3):
+    """The fp16 control path on one layer of the same workload: layer 0's
+    cache built once as int4 (s4kv_quantize_append) and once as fp16
+    (s4kv_fp16_append), then `calls` decode calls of each, interleaved, each
+    timed with HIP events on the call's stream; medians are reported."""
+    import torch
+    from int4_kivi_quantized_amd import Shape
+    from int4_kivi_quantized_amd.cache import Fp16LayerCache, LayerCache
+
+    ctx = W.context_lengths(wl)
+    plan = W.plan_pages(wl, ctx)
+    shape = Shape(wl.batch, wl.hq, wl.hkv, plan.num_pages, plan.max_pages)
+    bt = torch.from_numpy(plan.block_table).cuda()
+    mult = W.k_channel_multipliers(wl, 0)
+    ks, vs = [], []
+    for b in range(wl.batch):
+        k, v = W.sequence_kv(wl, 0, b, int(ctx[b]), "cuda", mult)
+        ks.append(k)
+        vs.append(v)
+    k_all, v_all = torch.cat(ks).contiguous(), torch.cat(vs).contiguous()
+    del ks, vs
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32), device="cuda")
+    sl = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+    q = W.queries(wl, 0, "cuda")
+    ctx_g = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    max_ctx = int(ctx.max())
+    # both caches resident, calls interleaved, so neither measurement sees a
+    # different allocation history or clock state than the other
+    caches = {"int4": LayerCache(shape), "fp16": Fp16LayerCache(shape)}
+    outs = {}
+    for name, cache in caches.items():
+        cache.append(k_all, v_all, cu, sl, int(ctx.max()), bt)
+        outs[name] = torch.empty_like(q)
+    del k_all, v_all
+    for _ in range(warmup):
+        for name, cache in caches.items():
+            cache.decode(q, bt, ctx_g, max_ctx, out=outs[name])
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(calls)] for name in caches}
+    torch.cuda.synchronize()
+    for i in range(calls):
+        for name, cache in caches.items():
+            a, b = ev[name][i]
+            a.record()
+            cache.decode(q, bt, ctx_g, max_ctx, out=outs[name])
+            b.record()
+    torch.cuda.synchronize()
+    res = {name: float(np.median([a.elapsed_time(b) for a, b in ev[name]])) for name in caches}
+    del caches, outs
+    torch.cuda.empty_cache()
+    f16_bytes = A.fp16_decode_bytes(ctx, wl.hq, wl.hkv)
+    i4_bytes = A.decode_bytes(ctx, wl.hq, wl.hkv)
+    return {
+        "workload": f"{wl.name}, layer 0 (no append)",
+        "calls": calls,
+        "fp16_call_ms": round(res["fp16"], 5),
+        "fp16_bytes_per_call": f16_bytes,
+        "fp16_gbs": round(f16_bytes / (res["fp16"] * 1e-3) / 1e9, 2),
+        "fp16_hbm_peak_frac": round(f16_bytes / (res["fp16"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "int4_call_ms": round(res["int4"], 5),
+        "int4_bytes_per_call": i4_bytes,
+        "bytes_ratio_fp16_over_int4": round(f16_bytes / i4_bytes, 4),
+        "int4_speedup_over_fp16": round(res["fp16"] / res["int4"], 4),
+    }
+
+
 def load_traffic(digest):
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if not os.path.exists(path):
@@ -335,6 +402,10 @@ def main():
             "prefill_quantize_gbs": None if r2["prefill_gbs"] is None else round(r2["prefill_gbs"], 2),
             "prefill_ms_per_layer": round(r2["prefill_ms_per_layer"], 4),
         }
+    if not args.no_secondary:
+        print("[bench] fp16 control", file=sys.stderr, flush=True)
+        line["fp16_control"] = fp16_control(wl)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -16,7 +16,9 @@
  *     page wait in an fp16 residual tail;
  *   - s4kv_paged_decode: one decode step of attention for every sequence over
  *     its int4 pages plus its fp16 tail (GQA, split over pages, cross-split
- *     softmax reduction).
+ *     softmax reduction);
+ *   - s4kv_fp16_append / s4kv_fp16_paged_decode: the same over an fp16 paged
+ *     cache, the control path the int4 cache is measured against.
  *
  * Quantizer (per group of fp16 values x): zero z = min(x) as fp16, scale
  * s = fp16((max - min) / 15) computed in fp32, code = clamp(rint_even((x - z)
@@ -162,6 +164,50 @@ s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void
                               const int32_t* block_table, const int32_t* ctx_lens,
                               int32_t max_ctx, float sm_scale, void* out, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* ---- fp16 control path ----
+ *
+ * The same cache and decode step with K and V kept in fp16 (the format the
+ * int4 cache replaces), for measuring the density / latency trade-off on the
+ * same harness: the S4 KV product page ("FAQ", the question on inference
+ * latency) says the int4 backend gives up some decode latency for density at
+ * long contexts, and the KV-quantization guide on adechristanto.de (section
+ * on separating weights, running state and reserved memory) notes that a
+ * smaller KV element halves the payload term but not necessarily latency.
+ *
+ * fp16 page format (pool fp16 [num_pages][num_kv_heads][4096]): per (page, KV
+ * head) the K block [16 tokens][128 channels], then the V block transposed,
+ * [128 channels][16 tokens]. There is no separate tail: a sequence's last
+ * page may be partial, and only its first ctx - 16 * (pages - 1) token slots
+ * are defined. Same shape rules, statuses and conventions as above. */
+#define S4KV_F16_CHUNK_BYTES 8192 /* bytes of one (page, KV head) fp16 chunk */
+
+/* Bytes of one layer's fp16 pool: num_pages * num_kv_heads * 8192; 0 if the
+ * shape is invalid. */
+size_t s4kv_fp16_pool_bytes(const s4kv_shape* shape);
+
+/* Append new K/V tokens to the fp16 pool of one layer.
+ * Args as s4kv_quantize_append (k, v fp16 [total_new][Hkv][128]; cu_new,
+ * slot, max_new, block_table); pages is the fp16 pool (written). Each new
+ * token t of sequence b goes to slot t % 16 of page block_table[b][t / 16].
+ * Device preconditions: as s4kv_quantize_append, without the tail ones.
+ * Returns S4KV_OK, an argument / shape error before any launch, or
+ * S4KV_ERR_HIP. */
+s4kv_status s4kv_fp16_append(const s4kv_shape* shape, const void* k, const void* v,
+                             const int32_t* cu_new, const int32_t* slot, int32_t max_new,
+                             const int32_t* block_table, void* pages, void* stream);
+
+/* One decode step over the fp16 pool: O[b][j] = sum_t softmax_t(sm_scale *
+ * q[b][j] . k_t) v_t over the ctx_lens[b] cached tokens. Args and workspace
+ * (s4kv_decode_workspace_bytes) as s4kv_paged_decode, without tails.
+ * Device preconditions: 1 <= ctx_lens[b] <= max_ctx and <= 16 *
+ * max_pages_per_seq; block ids of the ceil(ctx_lens[b] / 16) pages in
+ * [0, num_pages). A sequence with ctx_lens[b] <= 0 gets an all-zero output.
+ * Returns as s4kv_paged_decode. */
+s4kv_status s4kv_fp16_paged_decode(const s4kv_shape* shape, const void* q, const void* pages,
+                                   const int32_t* block_table, const int32_t* ctx_lens,
+                                   int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -54,3 +54,40 @@ class LayerCache:
         s = self.shape
         dims = (s.num_seqs, s.num_kv_heads, s.page_size, s.head_dim)
         return self.tail_k.view(*dims), self.tail_v.view(*dims)
+
+
+class Fp16LayerCache:
+    """One layer's fp16 paged cache (the control path): pool and workspace."""
+
+    def __init__(self, shape, device="cuda"):
+        if s4kv.s4kv_validate(shape) != s4kv.S4KV_OK:
+            raise s4kv.S4KVError(s4kv.s4kv_validate(shape), "Fp16LayerCache")
+        self.shape = shape
+        self.device = torch.device(device)
+        self.pages = torch.zeros(s4kv.s4kv_fp16_pool_bytes(shape) // 2, dtype=torch.float16,
+                                 device=self.device)
+        self._ws = None
+
+    def workspace(self, max_ctx):
+        need = s4kv.s4kv_decode_workspace_bytes(self.shape, max_ctx)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def append(self, k, v, cu_new, slot, max_new, block_table, stream=None):
+        s4kv.s4kv_fp16_append(self.shape, k, v, cu_new, slot, max_new, block_table, self.pages,
+                              stream)
+
+    def decode(self, q, block_table, ctx_lens, max_ctx, sm_scale=None, out=None, stream=None):
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(self.shape.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        s4kv.s4kv_fp16_paged_decode(self.shape, q, self.pages, block_table, ctx_lens, max_ctx,
+                                    sm_scale, out, self.workspace(max_ctx), stream)
+        return out
+
+    def chunk_view(self):
+        """fp16 [num_pages, Hkv, 4096] view of the pool."""
+        return self.pages.view(self.shape.num_pages, self.shape.num_kv_heads,
+                               s4kv.F16_CHUNK_BYTES // 2)

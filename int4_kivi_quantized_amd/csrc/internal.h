@@ -23,8 +23,25 @@ constexpr int kOffVScale = 2560;
 constexpr int kOffVZero = 2592;
 
 // Decode workspace: the total unit count, the waves sharing each (sequence, head)
-// and the per-(sequence, head, wave) partial results.
+// and the per-(sequence, head, wave) partial results. The int4 and fp16 decode
+// paths share it and the merge kernel.
 size_t workspace_bytes(const s4kv_shape& s);
+
+struct SplitWorkspace {
+  int32_t* total_units;  // [0]: units of the launch, written by wave 0
+  int32_t* seg_waves;    // [B * Hkv][2]: first / last wave sharing each (b, h)
+  float* slots;          // partial results, G x (128 outputs, m, l, 2 pad) floats per slot
+};
+SplitWorkspace split_workspace(const s4kv_shape& s, void* workspace);
+
+// Waves of the persistent decode grid: 8 per CU (two per SIMD).
+int resident_waves();
+
+// Merge the partial results of a decode stream launched with W waves into
+// fp16 out [B][Hq][128] (units per sequence: full pages plus one for a partial
+// one, as both decode paths count them).
+hipError_t launch_split_merge(const s4kv_shape& s, int W, int32_t max_ctx, const SplitWorkspace& ws,
+                              const int32_t* ctx_lens, void* out, hipStream_t stream);
 
 hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void* v,
                                   const int32_t* cu_new, const int32_t* slot, int32_t max_new,
@@ -36,5 +53,14 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q,
                                const int32_t* block_table, const int32_t* ctx_lens,
                                int32_t max_ctx, float sm_scale, void* out, void* workspace,
                                hipStream_t stream);
+
+// fp16 control path (fp16_decode.hip).
+constexpr int kF16ChunkHalves = 2 * S4KV_PAGE_SIZE * S4KV_HEAD_DIM;  // K block, then V^T block
+hipError_t launch_fp16_append(const s4kv_shape& s, const void* k, const void* v,
+                              const int32_t* cu_new, const int32_t* slot, int32_t max_new,
+                              const int32_t* block_table, void* pages, hipStream_t stream);
+hipError_t launch_fp16_decode(const s4kv_shape& s, const void* q, const void* pages,
+                              const int32_t* block_table, const int32_t* ctx_lens, int32_t max_ctx,
+                              float sm_scale, void* out, void* workspace, hipStream_t stream);
 
 }  // namespace s4kv

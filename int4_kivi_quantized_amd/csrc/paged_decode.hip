@@ -924,6 +924,21 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   *reinterpret_cast<uint2*>(o) = pk;
 }
 
+template <int G>
+hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages,
+                    const void* tail_k, const void* tail_v, const int32_t* block_table,
+                    const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves, float sm_scale,
+                    float* slots, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(W), dim3(64), 0, stream,
+                     static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
+                     static_cast<const __half*>(tail_k), static_cast<const __half*>(tail_v),
+                     block_table, ctx_lens, total_units, seg_waves, s.num_seqs, s.max_pages_per_seq,
+                     s.num_kv_heads, sm_scale, slots);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 int resident_waves() {
   // one wave per work-group, two per SIMD, four SIMDs per CU
   static int cached = 0;
@@ -940,25 +955,40 @@ int resident_waves() {
 
 // Workspace: [total units, padded to 256 B] [first / last wave per (b, h),
 // padded to 256 B] [partial slots].
+namespace {
 constexpr size_t kHeaderBytes = 256;
 size_t seg_bytes(const s4kv_shape& s) {
   return ((size_t)s.num_seqs * s.num_kv_heads * sizeof(int2) + 255) & ~size_t(255);
 }
+}  // namespace
 
-template <int G>
-hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages,
-                    const void* tail_k, const void* tail_v, const int32_t* block_table,
-                    const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves, float sm_scale,
-                    float* slots, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(W), dim3(64), 0, stream,
-                     static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
-                     static_cast<const __half*>(tail_k), static_cast<const __half*>(tail_v),
-                     block_table, ctx_lens, total_units, seg_waves, s.num_seqs, s.max_pages_per_seq,
-                     s.num_kv_heads, sm_scale, slots);
-  return hipGetLastError();
+SplitWorkspace split_workspace(const s4kv_shape& s, void* workspace) {
+  char* ws = static_cast<char*>(workspace);
+  SplitWorkspace w;
+  w.total_units = reinterpret_cast<int32_t*>(ws);
+  w.seg_waves = reinterpret_cast<int32_t*>(ws + kHeaderBytes);
+  w.slots = reinterpret_cast<float*>(ws + kHeaderBytes + seg_bytes(s));
+  return w;
 }
 
-}  // namespace
+hipError_t launch_split_merge(const s4kv_shape& s, int W, int32_t max_ctx, const SplitWorkspace& ws,
+                              const int32_t* ctx_lens, void* out, hipStream_t stream) {
+  // Slot groups per (sequence, head): about the number of waves that share a
+  // (b, h) when every context is max_ctx long (W waves over B * Hkv * pages
+  // units), rounded up to a power of two and capped by the block size. This
+  // only sizes the launch; any count of sharing waves is merged correctly.
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const int C = 32 * G;
+  const int64_t per_bh = ((int64_t)max_ctx + kPage - 1) / kPage;
+  const int64_t units = (int64_t)s.num_seqs * s.num_kv_heads * per_bh;
+  const int64_t share = (int64_t)W * per_bh / (units > 0 ? units : 1) + 2;
+  int R = 1;
+  while (R < share && 2 * R * C <= kReduceThreads) R *= 2;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads, s.num_seqs), dim3(C * R), 0,
+                     stream, ws.slots, ws.total_units, reinterpret_cast<const int2*>(ws.seg_waves), ctx_lens, s.max_pages_per_seq,
+                     s.num_kv_heads, G, W, static_cast<__half*>(out));
+  return hipGetLastError();
+}
 
 size_t workspace_bytes(const s4kv_shape& s) {
   const size_t nslots = (size_t)s.num_seqs * s.num_kv_heads + kMaxWaves;
@@ -971,16 +1001,13 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
                                const int32_t* block_table, const int32_t* ctx_lens,
                                int32_t max_ctx, float sm_scale, void* out, void* workspace,
                                hipStream_t stream) {
-  char* ws = static_cast<char*>(workspace);
-  int32_t* total_units = reinterpret_cast<int32_t*>(ws);
-  int2* seg_waves = reinterpret_cast<int2*>(ws + kHeaderBytes);
-  float* slots = reinterpret_cast<float*>(ws + kHeaderBytes + seg_bytes(s));
+  const SplitWorkspace ws = split_workspace(s, workspace);
   const int W = resident_waves();
   const int G = s.num_q_heads / s.num_kv_heads;
   hipError_t e = hipSuccess;
   switch (G) {
 #define S4KV_CASE(g) \
-  case g: e = launch_g<g>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, total_units, seg_waves, sm_scale, slots, stream); break;
+  case g: e = launch_g<g>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, ws.total_units, reinterpret_cast<int2*>(ws.seg_waves), sm_scale, ws.slots, stream); break;
     S4KV_CASE(1) S4KV_CASE(2) S4KV_CASE(3) S4KV_CASE(4) S4KV_CASE(5) S4KV_CASE(6) S4KV_CASE(7)
     S4KV_CASE(8) S4KV_CASE(9) S4KV_CASE(10) S4KV_CASE(11) S4KV_CASE(12) S4KV_CASE(13)
     S4KV_CASE(14) S4KV_CASE(15) S4KV_CASE(16)
@@ -988,20 +1015,7 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  // Slot groups per (sequence, head): about the number of waves that share a
-  // (b, h) when every context is max_ctx long (W waves over B * Hkv * pages
-  // units), rounded up to a power of two and capped by the block size. This
-  // only sizes the launch; any count of sharing waves is merged correctly.
-  const int C = 32 * G;
-  const int64_t per_bh = ((int64_t)max_ctx + kPage - 1) / kPage;
-  const int64_t units = (int64_t)s.num_seqs * s.num_kv_heads * per_bh;
-  const int64_t share = (int64_t)W * per_bh / (units > 0 ? units : 1) + 2;
-  int R = 1;
-  while (R < share && 2 * R * C <= kReduceThreads) R *= 2;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads, s.num_seqs), dim3(C * R), 0,
-                     stream, slots, total_units, seg_waves, ctx_lens, s.max_pages_per_seq,
-                     s.num_kv_heads, G, W, static_cast<__half*>(out));
-  return hipGetLastError();
+  return launch_split_merge(s, W, max_ctx, ws, ctx_lens, out, stream);
 }
 
 }  // namespace s4kv

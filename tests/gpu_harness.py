@@ -9,19 +9,22 @@ import torch
 import oracle
 import workload as W
 from int4_kivi_quantized_amd import Shape
-from int4_kivi_quantized_amd.cache import LayerCache
+from int4_kivi_quantized_amd.cache import Fp16LayerCache, LayerCache
 
 
 class LayerCase:
-    """One layer of a workload: the GPU cache and everything needed to check it."""
+    """One layer of a workload: the GPU cache and everything needed to check it.
 
-    def __init__(self, wl, layer=0, ctx_lens=None, extra_tokens=0, pool_seed_salt=None):
+    fp16=True builds the fp16 control cache (s4kv_fp16_*) instead of the int4 one."""
+
+    def __init__(self, wl, layer=0, ctx_lens=None, extra_tokens=0, pool_seed_salt=None, fp16=False):
+        self.fp16 = fp16
         self.wl = wl
         self.layer = layer
         self.ctx = np.asarray(W.context_lengths(wl) if ctx_lens is None else ctx_lens, dtype=np.int64)
         self.plan = W.plan_pages(wl, self.ctx, extra_tokens)
         self.shape = Shape(wl.batch, wl.hq, wl.hkv, self.plan.num_pages, self.plan.max_pages)
-        self.cache = LayerCache(self.shape)
+        self.cache = Fp16LayerCache(self.shape) if fp16 else LayerCache(self.shape)
         self.block_table = torch.from_numpy(self.plan.block_table).cuda()
         self.ctx_gpu = torch.from_numpy(self.ctx.astype(np.int32)).cuda()
         self.mult = W.k_channel_multipliers(wl, layer)
@@ -44,9 +47,13 @@ class LayerCase:
             cu = torch.tensor([0, wl.shared_prefix], dtype=torch.int32, device="cuda")
             sl = torch.zeros(1, dtype=torch.int32, device="cuda")
             from int4_kivi_quantized_amd import s4kv
-            s4kv.s4kv_quantize_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
-                                      wl.shared_prefix, bt, self.cache.pages, scratch.tail_k,
-                                      scratch.tail_v)
+            if self.fp16:
+                s4kv.s4kv_fp16_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
+                                      wl.shared_prefix, bt, self.cache.pages)
+            else:
+                s4kv.s4kv_quantize_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
+                                          wl.shared_prefix, bt, self.cache.pages, scratch.tail_k,
+                                          scratch.tail_v)
             for b in self.plan.sharing:
                 alias[b] = min(share_pages, int(self.ctx[b]) // wl.page)
         ks, vs, starts, counts = [], [], [], []
@@ -95,6 +102,12 @@ class LayerCase:
         """uint8 [full_b, Hkv, STRIDE] of sequence b's full pages."""
         full = int(self.ctx[b]) // self.wl.page
         ids = self.plan.block_table[b, :full]
+        return self.cache.chunk_view()[torch.from_numpy(ids.astype(np.int64)).cuda()].cpu().numpy()
+
+    def gpu_fp16_pages(self, b):
+        """fp16 [pages_b, Hkv, 4096] of sequence b's pages (fp16 cache)."""
+        n = -(-int(self.ctx[b]) // self.wl.page)
+        ids = self.plan.block_table[b, :n]
         return self.cache.chunk_view()[torch.from_numpy(ids.astype(np.int64)).cuda()].cpu().numpy()
 
     def gpu_tail(self, b):

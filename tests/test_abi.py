@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     text = open(os.path.join(ROOT, "include", "s4kv.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(s4kv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(s4kv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declarations_are_exported():
@@ -68,6 +68,8 @@ def test_null_shape_and_status_strings():
 def test_sizes():
     sh = Shape(**GOOD)
     assert s4kv.s4kv_pool_bytes(sh) == 100 * 8 * 2688
+    assert s4kv.s4kv_fp16_pool_bytes(sh) == 100 * 8 * 8192
+    assert s4kv.s4kv_fp16_pool_bytes(Shape(**{**GOOD, "page_size": 8})) == 0
     assert s4kv.s4kv_tail_bytes(sh) == 4 * 8 * 16 * 128 * 2
     assert s4kv.s4kv_pool_bytes(Shape(**{**GOOD, "head_dim": 64})) == 0
     ws = s4kv.s4kv_decode_workspace_bytes(sh, 1024)
@@ -123,4 +125,44 @@ def test_decode_refuses_before_launch():
     assert call(max_ctx=64 * 16 + 1) == s4kv.S4KV_ERR_INVALID_ARG
     assert call(ws_bytes=ws - 1) == s4kv.S4KV_ERR_WORKSPACE
     for i in range(6):
+        assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG
+
+
+def test_fp16_append_refuses_before_launch():
+    lib, P, fake = _raw_calls()
+    bad = Shape(**{**GOOD, "num_kv_heads": 5}).c()
+    good = Shape(**GOOD).c()
+    args = [fake, fake, fake, fake, 1, fake, fake, None]
+    assert lib.s4kv_fp16_append(ctypes.byref(bad), *args) == s4kv.S4KV_ERR_UNSUPPORTED
+    for i in (0, 1, 2, 3, 5, 6):
+        a = list(args)
+        a[i] = None
+        assert lib.s4kv_fp16_append(ctypes.byref(good), *a) == s4kv.S4KV_ERR_INVALID_ARG
+    a = list(args)
+    a[4] = 64 * 16 + 1
+    assert lib.s4kv_fp16_append(ctypes.byref(good), *a) == s4kv.S4KV_ERR_INVALID_ARG
+    a = list(args)
+    a[4] = 0
+    assert lib.s4kv_fp16_append(ctypes.byref(good), *a) == s4kv.S4KV_OK
+
+
+def test_fp16_decode_refuses_before_launch():
+    lib, P, fake = _raw_calls()
+    good = Shape(**GOOD).c()
+    ws = s4kv.s4kv_decode_workspace_bytes(Shape(**GOOD), 1000)
+
+    def call(shape=good, max_ctx=1000, ws_bytes=ws, null_at=None):
+        ptrs = [fake] * 4
+        if null_at is not None:
+            ptrs[null_at] = None
+        q, pages, bt, cl = ptrs
+        return lib.s4kv_fp16_paged_decode(ctypes.byref(shape), q, pages, bt, cl, max_ctx,
+                                          ctypes.c_float(0.088), fake, fake, ws_bytes, None)
+
+    bad = Shape(**{**GOOD, "head_dim": 64}).c()
+    assert call(shape=bad) == s4kv.S4KV_ERR_UNSUPPORTED
+    assert call(max_ctx=0) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(max_ctx=64 * 16 + 1) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 1) == s4kv.S4KV_ERR_WORKSPACE
+    for i in range(4):
         assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG

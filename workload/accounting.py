@@ -54,6 +54,17 @@ def decode_bytes(ctx_lens, num_q_heads, kv_heads):
                + 2 * (2 * b * num_q_heads * HEAD_DIM))
 
 
+def fp16_decode_bytes(ctx_lens, num_q_heads, kv_heads):
+    """Algorithmic HBM bytes of one fp16-cache decode launch (one layer): the
+    fp16 K and V of every cached token, one block-table entry per page (full
+    or partial), the context lengths, Q read and O written."""
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    b = len(ctx)
+    pages = -(-ctx // PAGE)
+    return int(kv_heads * ctx.sum() * FP16_TOKEN_BYTES + 4 * pages.sum() + 4 * b
+               + 2 * (2 * b * num_q_heads * HEAD_DIM))
+
+
 def quantize_bytes(n_tokens_flushed_pages, n_tail_tokens, kv_heads):
     """Algorithmic bytes of a bulk prefill quantize: fp16 K/V read for every
     token, int4 pages written for full pages, fp16 tail written."""
