@@ -20,6 +20,8 @@ s4kv_status check_shape(const s4kv_shape* s) {
   // launch-grid limits (y and z dimensions)
   if (s->num_kv_heads > 65535 || s->num_seqs > 65535 || s->num_q_heads > 65535)
     return S4KV_ERR_UNSUPPORTED;
+  // chunk indices (page * Hkv + head) must fit in int32
+  if ((int64_t)s->num_pages * s->num_kv_heads > INT32_MAX) return S4KV_ERR_INVALID_ARG;
   // token positions and the flat unit count (B * Hkv * (pages + 1)) must fit in int32
   if ((int64_t)s->max_pages_per_seq * S4KV_PAGE_SIZE > INT32_MAX) return S4KV_ERR_INVALID_ARG;
   if ((int64_t)s->num_seqs * s->num_kv_heads * ((int64_t)s->max_pages_per_seq + 1) > INT32_MAX)

@@ -329,8 +329,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // wave-uniform, so the range and cursor arithmetic stays scalar
     U = (int64_t)hkv * __builtin_amdgcn_readfirstlane(local);
   }
-  const int64_t u0 = (int64_t)w * U / W;
-  const int64_t u1 = (int64_t)(w + 1) * U / W;
+  // the 64-bit divisions run on the vector unit; bring the results back to
+  // scalar registers so every per-pair range check stays scalar
+  auto uniform64 = [](int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  const int64_t u0 = uniform64((int64_t)w * U / W);
+  const int64_t u1 = uniform64((int64_t)(w + 1) * U / W);
   const bool has_range = u0 < u1;
   if (w == 0 && lane == 0) total_units[0] = static_cast<int32_t>(U);
   if (!has_range) return;
@@ -374,7 +381,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int zrow = c >> 3;  // page of the K zeros this lane supplies (zero-term product)
   const float l2s = sm_scale * kLog2e;  // logits go to log2 units
   const float qk_scale = l2s * kQkUnscale;
-  const int64_t page_stride = (int64_t)hkv * kChunkStride;
 
   // ---- cursors over the wave's units (all fields wave-uniform) ----
   struct Cursor {
@@ -423,6 +429,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   __shared__ __align__(16) _Float16 tail_s[kPage][kHeadDim];  // fp16 tail V, one (b, h) at a time
   Cursor prod = start;
   int issued = 0, consumed = 0;
+  int pstage = 0, cstage = 0;  // ring slots of the next issue / the next consume
   auto q_row = [&](int b, int h) {
     return reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + h * G + head) * kHeadDim);
   };
@@ -437,7 +444,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   int nid_a = 0, nid_b = 0;
   auto prefetch_ids = [&]() {
     if (!next_pair(prod)) return;
-    const int32_t* bt = block_table + (int64_t)prod.b * max_pages + prod.unit;
+    // B * max_pages fits in int32 (the host checks B * Hkv * (max_pages + 1))
+    const int32_t* bt = block_table + (prod.b * max_pages + prod.unit);
     nid_a = bt[0];
     nid_b = (entry_pages(prod) == 2) ? bt[1] : nid_a;
   };
@@ -446,10 +454,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (prod.u >= u1) return;
     const int np = entry_pages(prod);
     const int idA = nid_a, idB = nid_b;
-    const int64_t head_off = (int64_t)prod.h * kChunkStride;
-    const uint8_t* chA = pages + idA * page_stride + head_off;
-    const uint8_t* chB = pages + idB * page_stride + head_off;
-    uint8_t* st = stage_s[issued % kStages];
+    // chunk index id * Hkv + h < num_pages * Hkv fits in 32 bits
+    const uint8_t* chA = pages + static_cast<uint64_t>(static_cast<uint32_t>(idA * hkv + prod.h)) * kChunkStride;
+    const uint8_t* chB = pages + static_cast<uint64_t>(static_cast<uint32_t>(idB * hkv + prod.h)) * kChunkStride;
+    uint8_t* st = stage_s[pstage];
+    if (++pstage == kStages) pstage = 0;
     dma16(chA + kOffKCodes + 16 * lane, st + 0);
     dma16(chB + kOffKCodes + 16 * lane, st + 1024);
     dma16(chA + kOffVCodes + 16 * lane, st + 2048);
@@ -824,7 +833,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     else if (after == 1) wait_vmcnt<kDmaPerStage>();
     else wait_vmcnt<0>();
     compiler_fence();
-    process_pair(stage_s[consumed % kStages], np == 2);
+    process_pair(stage_s[cstage], np == 2);
+    if (++cstage == kStages) cstage = 0;
     compiler_fence();
     ++consumed;
   };

@@ -48,6 +48,7 @@ GOOD = dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, num_pages=100, max_pages
     ({"num_q_heads": 128, "num_kv_heads": 8}, s4kv.S4KV_OK),   # G = 16
     ({"num_seqs": 0}, s4kv.S4KV_ERR_INVALID_ARG),
     ({"num_pages": 0}, s4kv.S4KV_ERR_INVALID_ARG),
+    ({"num_pages": 2**28, "num_kv_heads": 8, "num_q_heads": 32}, s4kv.S4KV_ERR_INVALID_ARG),  # chunk index > int32
     ({"max_pages_per_seq": -1}, s4kv.S4KV_ERR_INVALID_ARG),
     ({"num_kv_heads": 0}, s4kv.S4KV_ERR_INVALID_ARG),
 ])

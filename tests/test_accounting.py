@@ -54,3 +54,14 @@ def test_llama3_70b_layout_total():
     per_layer = A.cache_bytes(np.full(16, 32768), 8)
     assert per_layer == 16 * 8 * 2048 * 2624
     assert abs(80 * per_layer / 1e9 - 55.03) < 0.01
+
+
+def test_fp16_decode_bytes():
+    # fp16 control path: 512 B per token per KV head (the guide's payload with
+    # 2-byte elements), one block-table entry per page including a partial one
+    assert A.fp16_decode_bytes(np.array([37]), 12, 3) == 3 * 37 * 512 + 4 * 3 + 4 + 2 * (2 * 12 * 128)
+    assert A.fp16_decode_bytes(np.array([16, 1]), 4, 1) == 17 * 512 + 4 * 2 + 8 + 2 * (2 * 2 * 4 * 128)
+    # against the guide's payload formula for one layer
+    ctx = np.array([100, 2000, 4096])
+    kv = A.fp16_decode_bytes(ctx, 32, 8) - 4 * (-(-ctx // 16)).sum() - 4 * 3 - 2 * (2 * 3 * 32 * 128)
+    assert kv == A.fp16_kv_bytes(1, 8, 128, int(ctx.sum()))
