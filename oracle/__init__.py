@@ -20,6 +20,11 @@ Sources (cited by page title and section):
   Kernpunkte & Evidenz"): the cache is cut into fixed-size token pages
   (16 tokens) reached through a page table.
 
+* ``oracle.fp8``: the FP8 (E4M3) KV-cache variant with per-KV-head scales,
+  from the KV-quantization guide on adechristanto.de (sections on attention
+  arithmetic in the quantized domain and on default / calibrated scales) and
+  the OCP E4M3 format definition.
+
 Where the pages leave a step open, the oracle takes one plain reading; each
 reading is named in the docstring of the function that takes it.
 
