@@ -10,8 +10,9 @@ Headline workload: Llama-3.1-8B-shaped decode, 32 layers, 32 query / 8 KV
 heads, head_dim 128, batch 128, contexts U[2048, 8192], page 16.
 Secondary (same JSON line): Llama-3-70B-shaped decode, 80 layers, 64/8 heads,
 batch 16, 32768-token contexts, with the bulk prefill quantize of those
-contexts timed separately; and the fp16 control path (the same decode over an
-fp16 paged cache) against the int4 call on one layer of the headline workload.
+contexts timed separately; and the same decode call over this library's
+fp16 (control) and FP8 E4M3 caches against the int4 call, on one layer of the
+headline workload.
 
 Prints one JSON line. `value` is KV GB/s: the algorithmic bytes of all decode
 launches of a step (pages, tails, block-table entries, Q, O) divided by the
@@ -236,14 +237,17 @@ def copy_ceiling(nbytes=1 << 30, reps=10):
             "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 2)}
 
 
-def fp16_control(wl, calls=20, warmup=3):
-    """The fp16 control path on one layer of the same workload: layer 0's
-    cache built once as int4 (s4kv_quantize_append) and once as fp16
-    (s4kv_fp16_append), then `calls` decode calls of each, interleaved, each
-    timed with HIP events on the call's stream; medians are reported."""
+def format_comparison(wl, calls=20, warmup=3):
+    """The same decode over the three caches of this library on one layer of
+    the workload: layer 0's cache built as int4 (s4kv_quantize_append), as
+    fp16 (s4kv_fp16_append, the control path) and as FP8 E4M3
+    (s4kv_fp8_append, per-KV-head scales calibrated on sequence 0: its
+    largest magnitude over 448); then `calls` decode calls of each,
+    interleaved, each timed with HIP events on the call's stream; medians are
+    reported, with each format's algorithmic bytes per call."""
     import torch
     from int4_kivi_quantized_amd import Shape
-    from int4_kivi_quantized_amd.cache import Fp16LayerCache, LayerCache
+    from int4_kivi_quantized_amd.cache import Fp8LayerCache, Fp16LayerCache, LayerCache
 
     ctx = W.context_lengths(wl)
     plan = W.plan_pages(wl, ctx)
@@ -255,6 +259,8 @@ def fp16_control(wl, calls=20, warmup=3):
         k, v = W.sequence_kv(wl, 0, b, int(ctx[b]), "cuda", mult)
         ks.append(k)
         vs.append(v)
+    k_scale = ks[0].float().abs().amax(dim=(0, 2)) / 448.0
+    v_scale = vs[0].float().abs().amax(dim=(0, 2)) / 448.0
     k_all, v_all = torch.cat(ks).contiguous(), torch.cat(vs).contiguous()
     del ks, vs
     cu = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32), device="cuda")
@@ -262,9 +268,10 @@ def fp16_control(wl, calls=20, warmup=3):
     q = W.queries(wl, 0, "cuda")
     ctx_g = torch.from_numpy(ctx.astype(np.int32)).cuda()
     max_ctx = int(ctx.max())
-    # both caches resident, calls interleaved, so neither measurement sees a
-    # different allocation history or clock state than the other
-    caches = {"int4": LayerCache(shape), "fp16": Fp16LayerCache(shape)}
+    # all caches resident, calls interleaved, so no measurement sees a
+    # different allocation history or clock state than the others
+    caches = {"int4": LayerCache(shape), "fp16": Fp16LayerCache(shape),
+              "fp8": Fp8LayerCache(shape, k_scale.cpu(), v_scale.cpu())}
     outs = {}
     for name, cache in caches.items():
         cache.append(k_all, v_all, cu, sl, int(ctx.max()), bt)
@@ -286,20 +293,17 @@ def fp16_control(wl, calls=20, warmup=3):
     res = {name: float(np.median([a.elapsed_time(b) for a, b in ev[name]])) for name in caches}
     del caches, outs
     torch.cuda.empty_cache()
-    f16_bytes = A.fp16_decode_bytes(ctx, wl.hq, wl.hkv)
-    i4_bytes = A.decode_bytes(ctx, wl.hq, wl.hkv)
-    return {
-        "workload": f"{wl.name}, layer 0 (no append)",
-        "calls": calls,
-        "fp16_call_ms": round(res["fp16"], 5),
-        "fp16_bytes_per_call": f16_bytes,
-        "fp16_gbs": round(f16_bytes / (res["fp16"] * 1e-3) / 1e9, 2),
-        "fp16_hbm_peak_frac": round(f16_bytes / (res["fp16"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "int4_call_ms": round(res["int4"], 5),
-        "int4_bytes_per_call": i4_bytes,
-        "bytes_ratio_fp16_over_int4": round(f16_bytes / i4_bytes, 4),
-        "int4_speedup_over_fp16": round(res["fp16"] / res["int4"], 4),
-    }
+    nbytes = {"int4": A.decode_bytes(ctx, wl.hq, wl.hkv),
+              "fp16": A.fp16_decode_bytes(ctx, wl.hq, wl.hkv),
+              "fp8": A.fp8_decode_bytes(ctx, wl.hq, wl.hkv)}
+    out = {"workload": f"{wl.name}, layer 0 (no append)", "calls": calls}
+    for name in ("int4", "fp16", "fp8"):
+        gbs = nbytes[name] / (res[name] * 1e-3) / 1e9
+        out[name] = {"call_ms": round(res[name], 5), "bytes_per_call": nbytes[name],
+                     "gbs": round(gbs, 2), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    out["int4_speedup_over_fp16"] = round(res["fp16"] / res["int4"], 4)
+    out["int4_speedup_over_fp8"] = round(res["fp8"] / res["int4"], 4)
+    return out
 
 
 def load_traffic(digest):
@@ -403,8 +407,8 @@ def main():
             "prefill_ms_per_layer": round(r2["prefill_ms_per_layer"], 4),
         }
     if not args.no_secondary:
-        print("[bench] fp16 control", file=sys.stderr, flush=True)
-        line["fp16_control"] = fp16_control(wl)
+        print("[bench] format comparison (int4 / fp16 / fp8)", file=sys.stderr, flush=True)
+        line["format_comparison"] = format_comparison(wl)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -209,6 +209,64 @@ s4kv_status s4kv_fp16_paged_decode(const s4kv_shape* shape, const void* q, const
                                    int32_t max_ctx, float sm_scale, void* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* ---- FP8 (E4M3) paged cache ----
+ *
+ * The quantized KV cache the KV-quantization guide on adechristanto.de
+ * discusses most (sections on attention arithmetic in the quantized domain
+ * and on default or calibrated scales): every K and V element is one FP8
+ * byte, with scales of 1.0 by default or calibrated, per tensor or per
+ * attention head. Here: OCP E4M3 (1 sign, 4 exponent bits of bias 7, 3
+ * mantissa bits, largest finite 448, NaN = S.1111.111, no infinities) and one
+ * fp32 scale per KV head for K and one for V (equal values give a per-tensor
+ * scale). Queries stay fp16.
+ *
+ * Encode (append): y = fp16 input / scale as one IEEE fp32 division, then the
+ * nearest E4M3 value, ties to even; |y| >= 448 saturates to +-448 (0x7E /
+ * 0xFE); the sign is kept, also for a zero result. Decode: value(code) x scale.
+ *
+ * FP8 page format (pool uint8 [num_pages][num_kv_heads][4096]): per (page,
+ * KV head) four 1024-byte blocks in matrix-core operand order. With L = 16 g +
+ * c (g in 0..3, c in 0..15) and i in 0..15, byte 1024 j + 16 L + i holds
+ *   j = 0, 1:  K[token c][channel 32 (2j + i/8) + 8g + i%8]
+ *   j = 2, 3:  V[token 4g + i%4][channel 16 (4(j-2) + i/4) + c]
+ * As in the fp16 pool there is no tail: a sequence's last page may be
+ * partial, and only its first ctx - 16 * (pages - 1) token slots are defined.
+ * Same shape rules, statuses and conventions as above. */
+#define S4KV_FP8_CHUNK_BYTES 4096 /* bytes of one (page, KV head) FP8 chunk */
+
+/* Bytes of one layer's FP8 pool: num_pages * num_kv_heads * 4096; 0 if the
+ * shape is invalid. */
+size_t s4kv_fp8_pool_bytes(const s4kv_shape* shape);
+
+/* Quantize new K/V tokens to E4M3 and append them to the FP8 pool of one layer.
+ * Args as s4kv_fp16_append, plus (device pointers):
+ *   k_scale, v_scale  fp32 [num_kv_heads]: the scale of each KV head's K / V
+ *                     (finite, > 0; the caller keeps them fixed for the
+ *                     cache's lifetime, decode reads the same arrays).
+ *   pages             the FP8 pool (written).
+ * Each new token t of sequence b goes to slot t % 16 of page
+ * block_table[b][t / 16], in the layout above.
+ * Device preconditions: as s4kv_fp16_append.
+ * Returns S4KV_OK, an argument / shape error before any launch, or
+ * S4KV_ERR_HIP. */
+s4kv_status s4kv_fp8_append(const s4kv_shape* shape, const void* k, const void* v,
+                            const int32_t* cu_new, const int32_t* slot, int32_t max_new,
+                            const int32_t* block_table, const float* k_scale,
+                            const float* v_scale, void* pages, void* stream);
+
+/* One decode step over the FP8 pool: O[b][j] = sum_t softmax_t(sm_scale *
+ * q[b][j] . k_t) v_t over the ctx_lens[b] cached tokens, with k_t, v_t the
+ * E4M3 values times k_scale[h] / v_scale[h] (h = j / (Hq/Hkv)). Args and
+ * workspace (s4kv_decode_workspace_bytes) as s4kv_fp16_paged_decode, plus the
+ * scale arrays of s4kv_fp8_append (device, read only).
+ * Device preconditions: as s4kv_fp16_paged_decode.
+ * Returns as s4kv_paged_decode. */
+s4kv_status s4kv_fp8_paged_decode(const s4kv_shape* shape, const void* q, const void* pages,
+                                  const int32_t* block_table, const int32_t* ctx_lens,
+                                  int32_t max_ctx, float sm_scale, const float* k_scale,
+                                  const float* v_scale, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,3 +91,47 @@ class Fp16LayerCache:
         """fp16 [num_pages, Hkv, 4096] view of the pool."""
         return self.pages.view(self.shape.num_pages, self.shape.num_kv_heads,
                                s4kv.F16_CHUNK_BYTES // 2)
+
+
+class Fp8LayerCache:
+    """One layer's FP8 (E4M3) paged cache: pool, per-KV-head scales and workspace.
+
+    k_scale / v_scale: fp32 [Hkv] (or scalars, broadcast), fixed for the cache's
+    lifetime; 1.0 is the uncalibrated default."""
+
+    def __init__(self, shape, k_scale=1.0, v_scale=1.0, device="cuda"):
+        if s4kv.s4kv_validate(shape) != s4kv.S4KV_OK:
+            raise s4kv.S4KVError(s4kv.s4kv_validate(shape), "Fp8LayerCache")
+        self.shape = shape
+        self.device = torch.device(device)
+        self.pages = torch.zeros(s4kv.s4kv_fp8_pool_bytes(shape), dtype=torch.uint8,
+                                 device=self.device)
+        h = shape.num_kv_heads
+        self.k_scale = torch.as_tensor(k_scale, dtype=torch.float32).expand(h).contiguous().to(self.device)
+        self.v_scale = torch.as_tensor(v_scale, dtype=torch.float32).expand(h).contiguous().to(self.device)
+        self._ws = None
+
+    def workspace(self, max_ctx):
+        need = s4kv.s4kv_decode_workspace_bytes(self.shape, max_ctx)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def append(self, k, v, cu_new, slot, max_new, block_table, stream=None):
+        s4kv.s4kv_fp8_append(self.shape, k, v, cu_new, slot, max_new, block_table, self.k_scale,
+                             self.v_scale, self.pages, stream)
+
+    def decode(self, q, block_table, ctx_lens, max_ctx, sm_scale=None, out=None, stream=None):
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(self.shape.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        s4kv.s4kv_fp8_paged_decode(self.shape, q, self.pages, block_table, ctx_lens, max_ctx,
+                                   sm_scale, self.k_scale, self.v_scale, out,
+                                   self.workspace(max_ctx), stream)
+        return out
+
+    def chunk_view(self):
+        """uint8 [num_pages, Hkv, 4096] view of the pool."""
+        return self.pages.view(self.shape.num_pages, self.shape.num_kv_heads,
+                               s4kv.FP8_CHUNK_BYTES)

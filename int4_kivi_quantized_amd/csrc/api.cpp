@@ -133,4 +133,45 @@ s4kv_status s4kv_fp16_paged_decode(const s4kv_shape* shape, const void* q, const
   return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
 }
 
+size_t s4kv_fp8_pool_bytes(const s4kv_shape* shape) {
+  if (check_shape(shape) != S4KV_OK) return 0;
+  return (size_t)shape->num_pages * shape->num_kv_heads * S4KV_FP8_CHUNK_BYTES;
+}
+
+s4kv_status s4kv_fp8_append(const s4kv_shape* shape, const void* k, const void* v,
+                            const int32_t* cu_new, const int32_t* slot, int32_t max_new,
+                            const int32_t* block_table, const float* k_scale,
+                            const float* v_scale, void* pages, void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (max_new < 0) return S4KV_ERR_INVALID_ARG;
+  if (!k || !v || !cu_new || !slot || !block_table || !k_scale || !v_scale || !pages)
+    return S4KV_ERR_INVALID_ARG;
+  if (max_new == 0) return S4KV_OK;
+  if ((int64_t)max_new > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
+    return S4KV_ERR_INVALID_ARG;
+  const hipError_t e = s4kv::launch_fp8_append(*shape, k, v, cu_new, slot, max_new, block_table,
+                                               k_scale, v_scale, pages,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
+s4kv_status s4kv_fp8_paged_decode(const s4kv_shape* shape, const void* q, const void* pages,
+                                  const int32_t* block_table, const int32_t* ctx_lens,
+                                  int32_t max_ctx, float sm_scale, const float* k_scale,
+                                  const float* v_scale, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
+    return S4KV_ERR_INVALID_ARG;
+  if (!q || !pages || !block_table || !ctx_lens || !k_scale || !v_scale || !out || !workspace)
+    return S4KV_ERR_INVALID_ARG;
+  if (workspace_bytes < s4kv::workspace_bytes(*shape)) return S4KV_ERR_WORKSPACE;
+  const hipError_t e = s4kv::launch_fp8_decode(*shape, q, pages, block_table, ctx_lens, max_ctx,
+                                               sm_scale, k_scale, v_scale, out, workspace,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
 }  // extern "C"

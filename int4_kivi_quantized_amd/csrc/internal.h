@@ -54,7 +54,7 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q,
                                int32_t max_ctx, float sm_scale, void* out, void* workspace,
                                hipStream_t stream);
 
-// fp16 control path (fp16_decode.hip).
+// Dense paged caches (dense_decode.hip): fp16 control path and FP8 E4M3.
 constexpr int kF16ChunkHalves = 2 * S4KV_PAGE_SIZE * S4KV_HEAD_DIM;  // K block, then V^T block
 hipError_t launch_fp16_append(const s4kv_shape& s, const void* k, const void* v,
                               const int32_t* cu_new, const int32_t* slot, int32_t max_new,
@@ -62,5 +62,13 @@ hipError_t launch_fp16_append(const s4kv_shape& s, const void* k, const void* v,
 hipError_t launch_fp16_decode(const s4kv_shape& s, const void* q, const void* pages,
                               const int32_t* block_table, const int32_t* ctx_lens, int32_t max_ctx,
                               float sm_scale, void* out, void* workspace, hipStream_t stream);
+constexpr int kF8ChunkBytes = S4KV_FP8_CHUNK_BYTES;  // K blocks, then V blocks, operand order
+hipError_t launch_fp8_append(const s4kv_shape& s, const void* k, const void* v, const int32_t* cu_new,
+                             const int32_t* slot, int32_t max_new, const int32_t* block_table,
+                             const float* k_scale, const float* v_scale, void* pages, hipStream_t stream);
+hipError_t launch_fp8_decode(const s4kv_shape& s, const void* q, const void* pages,
+                             const int32_t* block_table, const int32_t* ctx_lens, int32_t max_ctx,
+                             float sm_scale, const float* k_scale, const float* v_scale, void* out,
+                             void* workspace, hipStream_t stream);
 
 }  // namespace s4kv

@@ -21,6 +21,7 @@ CHUNK_BYTES = 2624
 CHUNK_STRIDE = 2688
 MAX_GROUP = 16
 F16_CHUNK_BYTES = 8192  # fp16 control pool: K [16][128] then V^T [128][16] per (page, KV head)
+FP8_CHUNK_BYTES = 4096  # FP8 pool: E4M3 K and V per (page, KV head), operand order
 
 S4KV_OK = 0
 S4KV_ERR_INVALID_ARG = 1
@@ -103,6 +104,13 @@ def load():
     lib.s4kv_fp16_paged_decode.argtypes = [SP, P, P, P, P, I32, ctypes.c_float, P, P,
                                            ctypes.c_size_t, P]
     lib.s4kv_fp16_paged_decode.restype = ctypes.c_int
+    lib.s4kv_fp8_pool_bytes.argtypes = [SP]
+    lib.s4kv_fp8_pool_bytes.restype = ctypes.c_size_t
+    lib.s4kv_fp8_append.argtypes = [SP, P, P, P, P, I32, P, P, P, P, P]
+    lib.s4kv_fp8_append.restype = ctypes.c_int
+    lib.s4kv_fp8_paged_decode.argtypes = [SP, P, P, P, P, I32, ctypes.c_float, P, P, P, P,
+                                          ctypes.c_size_t, P]
+    lib.s4kv_fp8_paged_decode.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -111,6 +119,7 @@ EXPORTED = (
     "s4kv_validate", "s4kv_status_string", "s4kv_pool_bytes", "s4kv_tail_bytes",
     "s4kv_quantize_append", "s4kv_decode_workspace_bytes", "s4kv_paged_decode",
     "s4kv_fp16_pool_bytes", "s4kv_fp16_append", "s4kv_fp16_paged_decode",
+    "s4kv_fp8_pool_bytes", "s4kv_fp8_append", "s4kv_fp8_paged_decode",
 )
 
 
@@ -212,3 +221,34 @@ def s4kv_fp16_paged_decode(shape, q, pages, block_table, ctx_lens, max_ctx, sm_s
         int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "s4kv_fp16_paged_decode")
+
+
+def s4kv_fp8_pool_bytes(shape):
+    return load().s4kv_fp8_pool_bytes(ctypes.byref(shape.c()))
+
+
+def s4kv_fp8_append(shape, k, v, cu_new, slot, max_new, block_table, k_scale, v_scale, pages,
+                    stream=None):
+    """Quantize new K/V tokens (fp16 [total_new, Hkv, 128]) to E4M3 with the per-KV-head
+    scales (fp32 [Hkv]) and append them to the FP8 pool; see s4kv.h."""
+    import torch
+    st = load().s4kv_fp8_append(
+        ctypes.byref(shape.c()), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
+        _ptr(cu_new, torch.int32, "cu_new"), _ptr(slot, torch.int32, "slot"), int(max_new),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(k_scale, torch.float32, "k_scale"),
+        _ptr(v_scale, torch.float32, "v_scale"), _ptr(pages, torch.uint8, "pages"),
+        _stream(stream))
+    _check(st, "s4kv_fp8_append")
+
+
+def s4kv_fp8_paged_decode(shape, q, pages, block_table, ctx_lens, max_ctx, sm_scale, k_scale,
+                          v_scale, out, workspace, stream=None):
+    """One decode step over the FP8 pool: out fp16 [B, Hq, 128]; see s4kv.h."""
+    import torch
+    st = load().s4kv_fp8_paged_decode(
+        ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(pages, torch.uint8, "pages"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_lens, torch.int32, "ctx_lens"),
+        int(max_ctx), float(sm_scale), _ptr(k_scale, torch.float32, "k_scale"),
+        _ptr(v_scale, torch.float32, "v_scale"), _ptr(out, torch.float16, "out"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "s4kv_fp8_paged_decode")

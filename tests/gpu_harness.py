@@ -9,25 +9,52 @@ import torch
 import oracle
 import workload as W
 from int4_kivi_quantized_amd import Shape
-from int4_kivi_quantized_amd.cache import Fp16LayerCache, LayerCache
+from int4_kivi_quantized_amd.cache import Fp8LayerCache, Fp16LayerCache, LayerCache
+
+
+def calibrated_fp8_scales(wl, layer=0, mult=None, device="cuda"):
+    """Per-KV-head (k_scale, v_scale), fp32 [Hkv]: the largest magnitude of
+    sequence 0 (prefix included) over 448, so that the calibration sample just
+    fills the E4M3 range (the calibrated scales of the KV-quantization guide;
+    other sequences may exceed it and saturate)."""
+    n = int(W.context_lengths(wl)[0])
+    k, v = W.sequence_kv(wl, layer, 0, n, device, mult)
+    ks = k.float().abs().amax(dim=(0, 2)) / 448.0
+    vs = v.float().abs().amax(dim=(0, 2)) / 448.0
+    return ks.cpu().numpy().astype(np.float32), vs.cpu().numpy().astype(np.float32)
 
 
 class LayerCase:
     """One layer of a workload: the GPU cache and everything needed to check it.
 
-    fp16=True builds the fp16 control cache (s4kv_fp16_*) instead of the int4 one."""
+    kind: "int4" (s4kv_quantize_append / s4kv_paged_decode), "fp16" (the
+    control cache, s4kv_fp16_*) or "fp8" (s4kv_fp8_*, with per-KV-head scales
+    fp8_scales = (k_scale, v_scale); calibrated from sequence 0 by default)."""
 
-    def __init__(self, wl, layer=0, ctx_lens=None, extra_tokens=0, pool_seed_salt=None, fp16=False):
-        self.fp16 = fp16
+    def __init__(self, wl, layer=0, ctx_lens=None, extra_tokens=0, pool_seed_salt=None, kind="int4",
+                 fp8_scales=None):
+        assert kind in ("int4", "fp16", "fp8")
+        self.kind = kind
+        self.fp16 = kind == "fp16"
         self.wl = wl
         self.layer = layer
         self.ctx = np.asarray(W.context_lengths(wl) if ctx_lens is None else ctx_lens, dtype=np.int64)
         self.plan = W.plan_pages(wl, self.ctx, extra_tokens)
         self.shape = Shape(wl.batch, wl.hq, wl.hkv, self.plan.num_pages, self.plan.max_pages)
-        self.cache = Fp16LayerCache(self.shape) if fp16 else LayerCache(self.shape)
+        self.mult = W.k_channel_multipliers(wl, layer)
+        if kind == "fp8":
+            if fp8_scales is None:
+                fp8_scales = calibrated_fp8_scales(wl, layer, self.mult)
+            ks, vs = (np.broadcast_to(np.asarray(x, dtype=np.float32), (wl.hkv,)).copy()
+                      for x in fp8_scales)
+            self.k_scale, self.v_scale = ks, vs
+            self.cache = Fp8LayerCache(self.shape, torch.from_numpy(ks), torch.from_numpy(vs))
+        elif kind == "fp16":
+            self.cache = Fp16LayerCache(self.shape)
+        else:
+            self.cache = LayerCache(self.shape)
         self.block_table = torch.from_numpy(self.plan.block_table).cuda()
         self.ctx_gpu = torch.from_numpy(self.ctx.astype(np.int32)).cuda()
-        self.mult = W.k_channel_multipliers(wl, layer)
         self.q = W.queries(wl, layer, "cuda")
 
     # ------------------------------------------------------------- inputs
@@ -47,9 +74,13 @@ class LayerCase:
             cu = torch.tensor([0, wl.shared_prefix], dtype=torch.int32, device="cuda")
             sl = torch.zeros(1, dtype=torch.int32, device="cuda")
             from int4_kivi_quantized_amd import s4kv
-            if self.fp16:
+            if self.kind == "fp16":
                 s4kv.s4kv_fp16_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
                                       wl.shared_prefix, bt, self.cache.pages)
+            elif self.kind == "fp8":
+                s4kv.s4kv_fp8_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
+                                     wl.shared_prefix, bt, self.cache.k_scale, self.cache.v_scale,
+                                     self.cache.pages)
             else:
                 s4kv.s4kv_quantize_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
                                           wl.shared_prefix, bt, self.cache.pages, scratch.tail_k,
@@ -106,6 +137,12 @@ class LayerCase:
 
     def gpu_fp16_pages(self, b):
         """fp16 [pages_b, Hkv, 4096] of sequence b's pages (fp16 cache)."""
+        n = -(-int(self.ctx[b]) // self.wl.page)
+        ids = self.plan.block_table[b, :n]
+        return self.cache.chunk_view()[torch.from_numpy(ids.astype(np.int64)).cuda()].cpu().numpy()
+
+    def gpu_fp8_pages(self, b):
+        """uint8 [pages_b, Hkv, 4096] of sequence b's pages (FP8 cache)."""
         n = -(-int(self.ctx[b]) // self.wl.page)
         ids = self.plan.block_table[b, :n]
         return self.cache.chunk_view()[torch.from_numpy(ids.astype(np.int64)).cuda()].cpu().numpy()

@@ -88,3 +88,47 @@ def write_chunk(ck, sk, zk, cv, sv, zv):
     raw[OFF_VS:OFF_VS + 32] = np.asarray(sv, dtype=np.float16).view(np.uint8)
     raw[OFF_VZ:OFF_VZ + 32] = np.asarray(zv, dtype=np.float16).view(np.uint8)
     return raw
+
+
+# ---- FP8 (E4M3) pool: 4096 bytes per (page, KV head), operand order ----
+FP8_CHUNK_BYTES = 4096
+
+
+def fp8_byte_map():
+    """For each byte of an FP8 chunk: (is_v, token, channel), from the format
+    text: byte 1024 j + 16 L + i with L = 16 g + c holds K[c][32 (2j + i/8) +
+    8g + i%8] for j < 2 and V[4g + i%4][16 (4(j-2) + i/4) + c] for j >= 2."""
+    is_v = np.empty(FP8_CHUNK_BYTES, dtype=bool)
+    tok = np.empty(FP8_CHUNK_BYTES, dtype=np.int64)
+    ch = np.empty(FP8_CHUNK_BYTES, dtype=np.int64)
+    for j in range(4):
+        for L in range(64):
+            g, c = L // 16, L % 16
+            for i in range(16):
+                n = 1024 * j + 16 * L + i
+                if j < 2:
+                    is_v[n], tok[n], ch[n] = False, c, 32 * (2 * j + i // 8) + 8 * g + i % 8
+                else:
+                    is_v[n], tok[n], ch[n] = True, 4 * g + i % 4, 16 * (4 * (j - 2) + i // 4) + c
+    return is_v, tok, ch
+
+
+def read_fp8_chunks(raw):
+    """uint8 [..., 4096] -> (K codes, V codes), each uint8 [..., 16 tokens, 128 channels]."""
+    raw = np.asarray(raw, dtype=np.uint8)
+    is_v, tok, ch = fp8_byte_map()
+    lead = raw.shape[:-1]
+    k = np.zeros(lead + (PAGE, D), dtype=np.uint8)
+    v = np.zeros(lead + (PAGE, D), dtype=np.uint8)
+    k[..., tok[~is_v], ch[~is_v]] = raw[..., ~is_v]
+    v[..., tok[is_v], ch[is_v]] = raw[..., is_v]
+    return k, v
+
+
+def write_fp8_chunk(kc, vc):
+    """K and V codes uint8 [16, 128] -> one FP8 chunk, uint8 [4096]."""
+    is_v, tok, ch = fp8_byte_map()
+    out = np.empty(FP8_CHUNK_BYTES, dtype=np.uint8)
+    out[~is_v] = np.asarray(kc, dtype=np.uint8)[tok[~is_v], ch[~is_v]]
+    out[is_v] = np.asarray(vc, dtype=np.uint8)[tok[is_v], ch[is_v]]
+    return out

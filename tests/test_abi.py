@@ -71,6 +71,8 @@ def test_sizes():
     assert s4kv.s4kv_pool_bytes(sh) == 100 * 8 * 2688
     assert s4kv.s4kv_fp16_pool_bytes(sh) == 100 * 8 * 8192
     assert s4kv.s4kv_fp16_pool_bytes(Shape(**{**GOOD, "page_size": 8})) == 0
+    assert s4kv.s4kv_fp8_pool_bytes(sh) == 100 * 8 * 4096
+    assert s4kv.s4kv_fp8_pool_bytes(Shape(**{**GOOD, "num_q_heads": 12})) == 0
     assert s4kv.s4kv_tail_bytes(sh) == 4 * 8 * 16 * 128 * 2
     assert s4kv.s4kv_pool_bytes(Shape(**{**GOOD, "head_dim": 64})) == 0
     ws = s4kv.s4kv_decode_workspace_bytes(sh, 1024)
@@ -166,4 +168,45 @@ def test_fp16_decode_refuses_before_launch():
     assert call(max_ctx=64 * 16 + 1) == s4kv.S4KV_ERR_INVALID_ARG
     assert call(ws_bytes=ws - 1) == s4kv.S4KV_ERR_WORKSPACE
     for i in range(4):
+        assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG
+
+
+def test_fp8_append_refuses_before_launch():
+    lib, P, fake = _raw_calls()
+    bad = Shape(**{**GOOD, "page_size": 32}).c()
+    good = Shape(**GOOD).c()
+    # k, v, cu_new, slot, max_new, block_table, k_scale, v_scale, pages, stream
+    args = [fake, fake, fake, fake, 1, fake, fake, fake, fake, None]
+    assert lib.s4kv_fp8_append(ctypes.byref(bad), *args) == s4kv.S4KV_ERR_UNSUPPORTED
+    for i in (0, 1, 2, 3, 5, 6, 7, 8):
+        a = list(args)
+        a[i] = None
+        assert lib.s4kv_fp8_append(ctypes.byref(good), *a) == s4kv.S4KV_ERR_INVALID_ARG
+    a = list(args)
+    a[4] = -1
+    assert lib.s4kv_fp8_append(ctypes.byref(good), *a) == s4kv.S4KV_ERR_INVALID_ARG
+    a[4] = 64 * 16 + 1
+    assert lib.s4kv_fp8_append(ctypes.byref(good), *a) == s4kv.S4KV_ERR_INVALID_ARG
+    a[4] = 0
+    assert lib.s4kv_fp8_append(ctypes.byref(good), *a) == s4kv.S4KV_OK
+
+
+def test_fp8_decode_refuses_before_launch():
+    lib, P, fake = _raw_calls()
+    good = Shape(**GOOD).c()
+    ws = s4kv.s4kv_decode_workspace_bytes(Shape(**GOOD), 1000)
+
+    def call(shape=good, max_ctx=1000, ws_bytes=ws, null_at=None):
+        ptrs = [fake] * 8
+        if null_at is not None:
+            ptrs[null_at] = None
+        q, pages, bt, cl, ks, vs, out, wsp = ptrs
+        return lib.s4kv_fp8_paged_decode(ctypes.byref(shape), q, pages, bt, cl, max_ctx,
+                                         ctypes.c_float(0.088), ks, vs, out, wsp, ws_bytes, None)
+
+    assert call(shape=Shape(**{**GOOD, "num_q_heads": 8 * 17}).c()) == s4kv.S4KV_ERR_UNSUPPORTED
+    assert call(max_ctx=0) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(max_ctx=64 * 16 + 1) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 1) == s4kv.S4KV_ERR_WORKSPACE
+    for i in range(8):
         assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG

@@ -65,3 +65,15 @@ def test_fp16_decode_bytes():
     ctx = np.array([100, 2000, 4096])
     kv = A.fp16_decode_bytes(ctx, 32, 8) - 4 * (-(-ctx // 16)).sum() - 4 * 3 - 2 * (2 * 3 * 32 * 128)
     assert kv == A.fp16_kv_bytes(1, 8, 128, int(ctx.sum()))
+
+
+def test_fp8_decode_bytes():
+    # FP8 path: 256 B per token per KV head (one byte per element), one
+    # block-table entry per page, two fp32 scales per KV head
+    assert A.fp8_decode_bytes(np.array([37]), 12, 3) == 3 * 37 * 256 + 4 * 3 + 4 + 8 * 3 + 2 * (2 * 12 * 128)
+    ctx = np.array([100, 2000, 4096])
+    kv = (A.fp8_decode_bytes(ctx, 32, 8) - 4 * (-(-ctx // 16)).sum() - 4 * 3 - 8 * 8
+          - 2 * (2 * 3 * 32 * 128))
+    assert kv == A.fp16_kv_bytes(1, 8, 128, int(ctx.sum()), bytes_per_elem=1)
+    # half the fp16 payload
+    assert 2 * kv == A.fp16_kv_bytes(1, 8, 128, int(ctx.sum()))

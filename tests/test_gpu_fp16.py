@@ -25,7 +25,7 @@ def _print_case(name, **kw):
 
 
 def _case(wl, **kw):
-    case = LayerCase(wl, fp16=True, **kw)
+    case = LayerCase(wl, kind="fp16", **kw)
     case.cache.pages.fill_(float("nan"))
     case.prefill()
     return case
@@ -106,7 +106,7 @@ def test_fp16_decode_steps_with_append():
     wl = W.Workload("f16-8b-steps", 1, 8, base.hq, base.hkv, base.ctx, base.k_outliers, seed=base.seed)
     ctx0 = W.context_lengths(wl)
     steps = 20
-    case = LayerCase(wl, ctx_lens=ctx0, extra_tokens=steps, fp16=True)
+    case = LayerCase(wl, ctx_lens=ctx0, extra_tokens=steps, kind="fp16")
     case.cache.pages.fill_(float("nan"))
     case.prefill()
     new = []

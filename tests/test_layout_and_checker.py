@@ -78,3 +78,24 @@ def test_checker_catches_attention_faults():
     # a wrong softmax scale
     wrong = oracle.decode_attention(q, kh, vh, sm_scale=1.0 / math.sqrt(64))
     assert not parity.attention_ok(wrong, ref)[0]
+
+
+def test_fp8_byte_map_is_a_bijection():
+    is_v, tok, ch = layout.fp8_byte_map()
+    for v in (False, True):
+        cells = set(zip(tok[is_v == v].tolist(), ch[is_v == v].tolist()))
+        assert len(cells) == 16 * 128 and (is_v == v).sum() == 16 * 128
+    # a lane's 16 bytes of a K block are channels 32m + 8g .. +7 of one token, m = 2j, 2j + 1
+    assert list(ch[16 * 17:16 * 17 + 8]) == list(range(8, 16)) and set(tok[16 * 17:16 * 18]) == {1}
+    # a lane's V bytes 4t' .. 4t'+3 are tokens 4g .. 4g+3 of one channel
+    n = 2048 + 16 * 33 + 4
+    assert list(tok[n:n + 4]) == [8, 9, 10, 11] and set(ch[n:n + 4]) == {16 + 1}
+
+
+def test_fp8_write_read_roundtrip():
+    r = np.random.default_rng(0)
+    kc = r.integers(0, 256, (16, 128), dtype=np.uint8)
+    vc = r.integers(0, 256, (16, 128), dtype=np.uint8)
+    raw = layout.write_fp8_chunk(kc, vc)
+    k2, v2 = layout.read_fp8_chunks(raw[None])
+    assert np.array_equal(k2[0], kc) and np.array_equal(v2[0], vc)

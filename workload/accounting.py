@@ -65,6 +65,21 @@ def fp16_decode_bytes(ctx_lens, num_q_heads, kv_heads):
                + 2 * (2 * b * num_q_heads * HEAD_DIM))
 
 
+FP8_TOKEN_BYTES = 2 * HEAD_DIM                                                # K + V, 256
+
+
+def fp8_decode_bytes(ctx_lens, num_q_heads, kv_heads):
+    """Algorithmic HBM bytes of one FP8-cache decode launch (one layer): one
+    byte per cached K and V element (the guide's payload with 1-byte
+    elements), one block-table entry per page (full or partial), the context
+    lengths, the K and V scale of each KV head, Q read and O written."""
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    b = len(ctx)
+    pages = -(-ctx // PAGE)
+    return int(kv_heads * ctx.sum() * FP8_TOKEN_BYTES + 4 * pages.sum() + 4 * b + 8 * kv_heads
+               + 2 * (2 * b * num_q_heads * HEAD_DIM))
+
+
 def quantize_bytes(n_tokens_flushed_pages, n_tail_tokens, kv_heads):
     """Algorithmic bytes of a bulk prefill quantize: fp16 K/V read for every
     token, int4 pages written for full pages, fp16 tail written."""
