@@ -35,8 +35,11 @@
 //
 // Decode: the persistent split of the int4 path (a flat unit list over
 // (b, h, page), W equal contiguous ranges, partial results merged by the shared
-// merge kernel), one page per stage of an LDS DMA ring (16 KB per wave, 8
-// waves per CU).
+// merge kernel), whole pages per stage of an LDS DMA ring (each format sets
+// its stage count and pages per stage; 8 waves per CU). The DMA loads are
+// non-temporal. A single stage, refilled as soon as the wave has read it into
+// registers, measured fastest for both formats: more bytes in flight per wave
+// only queue longer.
 //  * logits: S^T[token][col] = sum_d K[token][d] q[d][col] on
 //    v_mfma_f32_16x16x32_f16, 4 per page; fp16 x fp16 products are exact in
 //    the fp32 sums, and E4M3 values convert to fp16 exactly.
@@ -99,9 +102,14 @@ __device__ inline float xor8(float v) {
   return bitsf(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(fbits(v)), 0x128, 0xF, 0xF, true)));
 }
 
+// Every cache byte is read once: the loads carry the non-temporal policy (nt),
+// which streams them past the caches; on MI355X a pure read of 4 KB chunks
+// runs at about 6.8-7.0 TB/s this way against about 6.0 TB/s without it.
+constexpr int kNonTemporal = 2;
 __device__ inline void dma16(const uint8_t* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
-                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0,
+                                   kNonTemporal);
 }
 // s_waitcnt with only vmcnt constrained (gfx9 encoding)
 template <int N>
@@ -133,7 +141,9 @@ __device__ inline void compiler_fence() { __asm__ __volatile__("" ::: "memory");
 
 struct F16Pages {
   static constexpr int kChunk = kF16ChunkHalves * 2;  // 8192
-  static constexpr int kStages = 2;
+  static constexpr int kStages = 1;
+  static constexpr int kPagesPerStage = 1;
+  static constexpr int kWavesPerSimd = 2;
   static constexpr bool kScaled = false;
   struct Stage {
     u4 k[4];  // K[token c][32m + 8g .. +7], m = 0..3
@@ -178,7 +188,9 @@ __device__ inline h2 e4m3_hi(uint32_t w) { return __builtin_amdgcn_cvt_scalef32_
 
 struct F8Pages {
   static constexpr int kChunk = kF8ChunkBytes;  // 4096
-  static constexpr int kStages = 4;
+  static constexpr int kStages = 1;
+  static constexpr int kPagesPerStage = 1;
+  static constexpr int kWavesPerSimd = 2;
   static constexpr bool kScaled = true;
   struct Stage {
     u4 b[4];  // the lane's 16 bytes of blocks 0..3
@@ -192,6 +204,24 @@ struct F8Pages {
         "ds_read_b128 %3, %4 offset:3072\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r.b[0]), "=&v"(r.b[1]), "=&v"(r.b[2]), "=&v"(r.b[3])
+        : "v"(a)
+        : "memory");
+  }
+  // two consecutive pages of a stage
+  __device__ static void read2(uint32_t base, int lane, Stage& r, Stage& s) {
+    const uint32_t a = base + 16 * lane;
+    __asm__ __volatile__(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r.b[0]), "=&v"(r.b[1]), "=&v"(r.b[2]), "=&v"(r.b[3]), "=&v"(s.b[0]), "=&v"(s.b[1]),
+          "=&v"(s.b[2]), "=&v"(s.b[3])
         : "v"(a)
         : "memory");
   }
@@ -223,7 +253,7 @@ __device__ inline int owner_wave(int64_t u, int64_t U, int W) {
 }
 
 template <class Fmt, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dense_stream_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Fmt::kWavesPerSimd, Fmt::kWavesPerSimd))) void dense_stream_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
     int32_t* __restrict__ total_units, int2* __restrict__ seg_waves, int32_t B, int32_t max_pages,
@@ -232,7 +262,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   constexpr bool kSplitCols = (G <= 8);  // columns c and c + 8: hi / lo parts of one head
   constexpr int kChunk = Fmt::kChunk;
   constexpr int kStages = Fmt::kStages;
-  constexpr int kDmaPerStage = kChunk / 1024;
+  constexpr int kPer = Fmt::kPagesPerStage;  // pages of one (b, h) per ring stage
+  static_assert(kPer == 1 || kPer == 2, "one or two pages per stage");
+  constexpr int kDmaPerStage = kPer * kChunk / 1024;
   const int w = blockIdx.x, W = gridDim.x;
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
@@ -315,24 +347,46 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
   };
 
-  // ---- DMA ring: one page per stage ----
-  __shared__ __align__(16) uint8_t stage_s[kStages][kChunk];
+  // ---- DMA ring: kPer pages of one (b, h) per stage ----
+  // With two pages per stage, a stage whose segment has one page left holds
+  // that page twice (the second copy comes from L2 and is fully masked), so
+  // every stage is the same number of DMA operations.
+  __shared__ __align__(16) uint8_t stage_s[kStages][kPer * kChunk];
   Cursor prod = start;
   int issued = 0, consumed = 0;
-  int nid = 0;  // block id of the page at the producer cursor, loaded one page ahead
+  // block ids of the pages at the producer cursor, loaded one stage ahead
+  int nid = 0, nid2 = 0;
   auto prefetch_id = [&]() {
-    if (prod.u < u1)
-      nid = block_table[(int64_t)__builtin_amdgcn_readfirstlane(prod.b) * max_pages +
-                        __builtin_amdgcn_readfirstlane(prod.unit)];
+    if (prod.u < u1) {
+      const int64_t row = (int64_t)__builtin_amdgcn_readfirstlane(prod.b) * max_pages;
+      const int un = __builtin_amdgcn_readfirstlane(prod.unit);
+      nid = block_table[row + un];
+      if constexpr (kPer == 2) nid2 = (un + 1 < prod.npages) ? block_table[row + un + 1] : nid;
+    }
   };
+  // the second page of a stage exists when the cursor, moved past the first,
+  // is still inside the range and the same (b, h)
+  auto has_second = [&](const Cursor& cu) { return cu.u < u1 && cu.unit != 0; };
   auto produce = [&]() {
     if (prod.u >= u1) return;
-    const uint8_t* ch = pages + nid * page_stride + (int64_t)prod.h * kChunk + 16 * lane;
+    const int64_t head_off = (int64_t)prod.h * kChunk + 16 * lane;
+    const uint8_t* ch = pages + nid * page_stride + head_off;
+    const uint8_t* ch2 = ch;
+    advance(prod);
+    if constexpr (kPer == 2) {
+      if (has_second(prod)) {
+        ch2 = pages + nid2 * page_stride + head_off;
+        advance(prod);
+      }
+    }
     uint8_t* st = stage_s[issued % kStages];
 #pragma unroll
-    for (int i = 0; i < kDmaPerStage; ++i) dma16(ch + 1024 * i, st + 1024 * i);
+    for (int i = 0; i < kChunk / 1024; ++i) dma16(ch + 1024 * i, st + 1024 * i);
+    if constexpr (kPer == 2) {
+#pragma unroll
+      for (int i = 0; i < kChunk / 1024; ++i) dma16(ch2 + 1024 * i, st + kChunk + 1024 * i);
+    }
     ++issued;
-    advance(prod);
     prefetch_id();
   };
 
@@ -384,23 +438,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   auto lds_addr = [&](const uint8_t* p) -> uint32_t {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
   };
-  // n_valid: defined tokens of this page (16 except a sequence's last page)
-  auto process_page = [&](const uint8_t* st, int n_valid) {
-    typename Fmt::Stage r;
-    Fmt::read(lds_addr(st), lane, r);
+  // n_valid[pg]: defined tokens of page pg of the stage (16, fewer on a
+  // sequence's last page, 0 for the repeated copy of a lone page)
+  auto process_stage = [&](const uint8_t* st, const int (&n_valid)[kPer]) {
+    typename Fmt::Stage r[kPer];
+    if constexpr (kPer == 2) Fmt::read2(lds_addr(st), lane, r[0], r[1]);
+    else Fmt::read(lds_addr(st), lane, r[0]);
     // the stage is in registers: refill it at once
     compiler_fence();
     produce();
     compiler_fence();
-    h8 km[4];
-    Fmt::keys(r, km);
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lg[kPer][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc = mfma32(km[m], qv[m], acc);
-    float lg[4];
+    for (int pg = 0; pg < kPer; ++pg) {
+      h8 km[4];
+      Fmt::keys(r[pg], km);
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[i] = (4 * g + i < n_valid) ? acc[i] * l2s : kNegInf;
-    const float mb = rows_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
+      for (int m = 0; m < 4; ++m) acc = mfma32(km[m], qv[m], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[pg][i] = (4 * g + i < n_valid[pg]) ? acc[i] * l2s : kNegInf;
+    }
+    float mx = fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3]));
+#pragma unroll
+    for (int pg = 1; pg < kPer; ++pg)
+      mx = fmaxf(mx, fmaxf(fmaxf(lg[pg][0], lg[pg][1]), fmaxf(lg[pg][2], lg[pg][3])));
+    const float mb = rows_max(mx);
     const bool up = mb > m_run + kLazyRescale;
     if (__any(up)) {
       const float mnew = up ? mb : m_run;
@@ -411,43 +474,46 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       m_run = mnew;
     }
     const float ms = (m_run == kNegInf) ? 0.f : m_run;
-    h4 bh, bl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(lg[i] - ms);
-      l_part += p;
-      const _Float16 ph = static_cast<_Float16>(p);
-      bh[i] = ph;
-      bl[i] = static_cast<_Float16>(p - static_cast<float>(ph));
-    }
-    h4 vt[8];
-    Fmt::values(r, vt);
-    if (n_valid < kPage) {
-      // undefined slots of a partial page: their probabilities are 0, and
-      // their values must not be NaN or Inf either
+    for (int pg = 0; pg < kPer; ++pg) {
+      h4 bh, bl;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(lg[pg][i] - ms);
+        l_part += p;
+        const _Float16 ph = static_cast<_Float16>(p);
+        bh[i] = ph;
+        bl[i] = static_cast<_Float16>(p - static_cast<float>(ph));
+      }
+      h4 vt[8];
+      Fmt::values(r[pg], vt);
+      if (n_valid[pg] < kPage) {
+        // undefined slots of a partial page: their probabilities are 0, and
+        // their values must not be NaN or Inf either
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * g + i >= n_valid) vt[t][i] = static_cast<_Float16>(0.f);
-    }
-    if constexpr (kSplitCols) {
-      const h4 b = lo_col ? bl : bh;
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) o[t] = mfma16(vt[t], b, o[t]);
-    } else {
+          for (int i = 0; i < 4; ++i)
+            if (4 * g + i >= n_valid[pg]) vt[t][i] = static_cast<_Float16>(0.f);
+      }
+      if constexpr (kSplitCols) {
+        const h4 b = lo_col ? bl : bh;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        o[t] = mfma16(vt[t], bh, o[t]);
-        o[t] = mfma16(vt[t], bl, o[t]);
+        for (int t = 0; t < 8; ++t) o[t] = mfma16(vt[t], b, o[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          o[t] = mfma16(vt[t], bh, o[t]);
+          o[t] = mfma16(vt[t], bl, o[t]);
+        }
       }
     }
   };
 
   // ---- main stream ----
-  // kStages pages are issued ahead; loads complete in issue order, so "at
-  // most kDmaPerStage x (pages issued after this one)" outstanding
-  // vector-memory operations means this page has landed. Other outstanding
+  // kStages stages are issued ahead; loads complete in issue order, so "at
+  // most kDmaPerStage x (stages issued after this one)" outstanding
+  // vector-memory operations means this stage has landed. Other outstanding
   // operations (query loads, partial stores) can only make the wait stricter.
   prefetch_id();
 #pragma unroll
@@ -456,13 +522,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   while (cons.u < u1) {
     begin_segment(cons);
     do {
-      const int n_valid = (cons.unit == cons.npages - 1) ? cons.last_n : kPage;
+      // the consumer walks the same stage boundaries as the producer
+      int n_valid[kPer];
+      n_valid[0] = (cons.unit == cons.npages - 1) ? cons.last_n : kPage;
+      advance(cons);
+      if constexpr (kPer == 2) {
+        n_valid[1] = 0;
+        if (has_second(cons)) {
+          n_valid[1] = (cons.unit == cons.npages - 1) ? cons.last_n : kPage;
+          advance(cons);
+        }
+      }
       wait_pages_after<kDmaPerStage, kStages - 1>(issued - consumed - 1);
       compiler_fence();
-      process_page(stage_s[consumed % kStages], n_valid);
+      process_stage(stage_s[consumed % kStages], n_valid);
       compiler_fence();
       ++consumed;
-      advance(cons);
     } while (cons.u < u1 && cons.b == cur_b && cons.h == cur_h);
     end_segment();
   }
@@ -573,7 +648,8 @@ hipError_t launch_dense_decode(const s4kv_shape& s, const void* q, const void* p
                                float sm_scale, const float* k_scale, const float* v_scale, void* out,
                                void* workspace, hipStream_t stream) {
   const SplitWorkspace ws = split_workspace(s, workspace);
-  const int W = resident_waves();
+  // resident_waves() is two per SIMD
+  const int W = min(resident_waves() / 2 * Fmt::kWavesPerSimd, kMaxWaves);
   const int G = s.num_q_heads / s.num_kv_heads;
   hipError_t e = hipSuccess;
   switch (G) {

@@ -36,6 +36,9 @@ SplitWorkspace split_workspace(const s4kv_shape& s, void* workspace);
 
 // Waves of the persistent decode grid: 8 per CU (two per SIMD).
 int resident_waves();
+// Upper bound on any persistent decode grid; the workspace holds partial-result
+// slots for this many waves.
+constexpr int kMaxWaves = 4096;
 
 // Merge the partial results of a decode stream launched with W waves into
 // fp16 out [B][Hq][128] (units per sequence: full pages plus one for a partial

@@ -64,7 +64,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // is c * p * s * 2^-24.
 constexpr float kQkUnscale = 268435456.0f;  // 2^28
 constexpr float kPvUnscale = 16777216.0f;   // 2^24
-constexpr int kMaxWaves = 4096;             // upper bound on the persistent grid
 // A V scale is at most (65504 + 65504) / 15 < 2^13.1 and fp16 holds values
 // below 2^16, so p * sV stays finite while p <= 2^2.
 constexpr float kLazyRescale = 2.0f;
@@ -177,12 +176,20 @@ __device__ inline void zero_terms(const h8 (&qh)[4], const u4 (&z)[4], float& ta
 //   [4096,4608) K scale+zero A     [4608,5120) K scale+zero B
 //   [5120,5184) V scale+zero A     [5184,5248) V scale+zero B
 constexpr int kStageBytes = 5248;
-constexpr int kStages = 3;          // every stage in flight while a pair is computed
+// One stage: the wave reads it into registers and refills it at once, so the
+// next pair loads while this one is computed. Deeper rings measured slower
+// (more bytes in flight per wave only queue longer).
+constexpr int kStages = 1;
 constexpr int kDmaPerStage = 6;     // DMA instructions issued per stage
 
+// Every cache byte is read once: the loads carry the non-temporal policy (nt),
+// which streams them past the caches; on MI355X a pure read of 4 KB chunks
+// runs at about 6.8-7.0 TB/s this way against about 6.0 TB/s without it.
+constexpr int kNonTemporal = 2;
 __device__ inline void dma16(const uint8_t* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
-                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0,
+                                   kNonTemporal);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -191,6 +198,20 @@ template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// Wait until the oldest stage in flight has landed, when `ahead` later stages
+// (Per DMA operations each) may stay outstanding.
+template <int Per, int MaxAhead>
+__device__ inline void wait_pages_after(int ahead) {
+  if constexpr (MaxAhead > 0) {
+    if (ahead >= MaxAhead) {
+      wait_vmcnt<Per * MaxAhead>();
+      return;
+    }
+    wait_pages_after<Per, MaxAhead - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
+  }
 }
 // wait for all LDS / scalar-memory operations of this wave
 __device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
@@ -681,8 +702,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         (const __attribute__((address_space(3))) uint8_t*)(p)));
   };
   // The stage just read into registers (its asm block ended with
-  // lgkmcnt(0)) is free: refill it with the next pair at once, so three pairs
-  // are in flight while this one is computed.
+  // lgkmcnt(0)) is free: refill it with the next pair at once, so kStages
+  // pairs are in flight while this one is computed.
   auto refill = [&]() {
     compiler_fence();
     produce();
@@ -822,16 +843,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   // ---- main stream ----
-  // Three pairs are issued ahead. vmcnt counts this wave's outstanding
+  // kStages pairs are issued ahead. vmcnt counts this wave's outstanding
   // vector-memory operations and loads complete in issue order, so "at most
   // 6 x (pairs issued after this one)" outstanding means this pair has landed
   // in LDS; other outstanding operations (query and tail loads,
   // partial-result stores) can only make the wait stricter.
   auto consume_pair = [&](int np) {
-    const int after = issued - consumed - 1;
-    if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
-    else if (after == 1) wait_vmcnt<kDmaPerStage>();
-    else wait_vmcnt<0>();
+    wait_pages_after<kDmaPerStage, kStages - 1>(issued - consumed - 1);
     compiler_fence();
     process_pair(stage_s[cstage], np == 2);
     if (++cstage == kStages) cstage = 0;
@@ -839,9 +857,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     ++consumed;
   };
   prefetch_ids();
-  produce();
-  produce();
-  produce();
+#pragma unroll
+  for (int s = 0; s < kStages; ++s) produce();
   Cursor cons = start;
   while (cons.u < u1) {
     begin_segment(cons);
