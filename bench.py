@@ -14,6 +14,10 @@ contexts timed separately; and the same decode call over this library's
 fp16 (control) and FP8 E4M3 caches against the int4 call, on one layer of the
 headline workload.
 
+Two ceilings frame the decode call's rate: a copy (torch, read + write) and
+the library's read probe (s4kv_probe_read: random 4 KB chunks through the
+decode kernels' own load path, with and without the non-temporal policy).
+
 Prints one JSON line. `value` is KV GB/s: the algorithmic bytes of all decode
 launches of a step (pages, tails, block-table entries, Q, O) divided by the
 step time.
@@ -237,6 +241,44 @@ def copy_ceiling(nbytes=1 << 30, reps=10):
             "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 2)}
 
 
+def read_ceiling(reps=10):
+    """What the decode kernels' load path sustains with nothing attached:
+    s4kv_probe_read over 2 GiB in 4096-byte chunks taken in a random order,
+    one wave per work-group, 8 per CU (the decode grid), one chunk in flight
+    per wave; with and without the non-temporal policy the decode kernels use.
+    Medians of `reps` calls timed with HIP events."""
+    import torch
+    from int4_kivi_quantized_amd import s4kv
+    pool_bytes = 2 << 30
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    chunks = pool_bytes // 4096
+    waves = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    per = chunks // waves
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    ids = torch.randperm(chunks, generator=g, device="cuda", dtype=torch.int64)[:waves * per]
+    ids = ids.to(torch.int32).contiguous()
+    out = {"chunk_bytes": 4096, "order": "random", "waves": waves,
+           "bytes_read": waves * per * 4096}
+    for nt in (True, False):
+        s4kv.s4kv_probe_read(pool, ids, per, waves, nt)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            s4kv.s4kv_probe_read(pool, ids, per, waves, nt)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        key = "non_temporal" if nt else "default_policy"
+        out[key] = {"avg_ms": round(ms, 5), "gbs": round(out["bytes_read"] / (ms * 1e-3) / 1e9, 1)}
+    del pool, ids
+    torch.cuda.empty_cache()
+    out["gbs"] = out["non_temporal"]["gbs"]
+    return out
+
+
 def format_comparison(wl, calls=20, warmup=3):
     """The same decode over the three caches of this library on one layer of
     the workload: layer 0's cache built as int4 (s4kv_quantize_append), as
@@ -348,6 +390,9 @@ def main():
           f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     copy = copy_ceiling()
     print(f"[bench] copy ceiling {copy['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    rceil = read_ceiling()
+    print(f"[bench] read ceiling {rceil['gbs']:.0f} GB/s (non-temporal), "
+          f"{rceil['default_policy']['gbs']:.0f} GB/s (default policy)", file=sys.stderr, flush=True)
     r = run_decode_bench(wl, args.steps, args.warmup, append=wl.append)
     del r["model"]
     torch.cuda.empty_cache()
@@ -388,8 +433,10 @@ def main():
             "bytes_per_launch": int(r["decode_launch_bytes"]),
             "traffic": (traffic or {}).get("hbm_bytes_per_launch"),
             "frac_of_copy_ceiling": round(r["decode_launch_gbs"] / copy["gbs"], 4),
+            "frac_of_read_ceiling": round(r["decode_launch_gbs"] / rceil["gbs"], 4),
         },
         "copy_ceiling": copy,
+        "read_ceiling": rceil,
     }
     if not args.no_secondary and wl.name != "llama3-70b":
         wl2 = W.WORKLOADS["llama3-70b"]

@@ -111,6 +111,8 @@ def load():
     lib.s4kv_fp8_paged_decode.argtypes = [SP, P, P, P, P, I32, ctypes.c_float, P, P, P, P,
                                           ctypes.c_size_t, P]
     lib.s4kv_fp8_paged_decode.restype = ctypes.c_int
+    lib.s4kv_probe_read.argtypes = [P, ctypes.c_size_t, P, I32, I32, I32, P]
+    lib.s4kv_probe_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -120,6 +122,7 @@ EXPORTED = (
     "s4kv_quantize_append", "s4kv_decode_workspace_bytes", "s4kv_paged_decode",
     "s4kv_fp16_pool_bytes", "s4kv_fp16_append", "s4kv_fp16_paged_decode",
     "s4kv_fp8_pool_bytes", "s4kv_fp8_append", "s4kv_fp8_paged_decode",
+    "s4kv_probe_read",
 )
 
 
@@ -252,3 +255,13 @@ def s4kv_fp8_paged_decode(shape, q, pages, block_table, ctx_lens, max_ctx, sm_sc
         _ptr(v_scale, torch.float32, "v_scale"), _ptr(out, torch.float16, "out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "s4kv_fp8_paged_decode")
+
+
+def s4kv_probe_read(pool, chunk_ids, chunks_per_wave, waves, non_temporal=True, stream=None):
+    """Read 4096-byte chunks of pool (uint8) with the decode kernels' load path;
+    a measurement aid, see include/s4kv_probe.h."""
+    import torch
+    st = load().s4kv_probe_read(
+        _ptr(pool, torch.uint8, "pool"), pool.numel(), _ptr(chunk_ids, torch.int32, "chunk_ids"),
+        int(chunks_per_wave), int(waves), 1 if non_temporal else 0, _stream(stream))
+    _check(st, "s4kv_probe_read")

@@ -15,7 +15,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    text = open(os.path.join(ROOT, "include", "s4kv.h")).read()
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc))
+                   if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(s4kv_[a-z0-9_]+)\s*\(", text)))
 
@@ -25,7 +27,7 @@ def test_header_declarations_are_exported():
     names = _declared()
     assert len(names) >= 7
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in s4kv.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/*.h but not exported"
     assert set(names) == set(s4kv.EXPORTED)
 
 
@@ -210,3 +212,12 @@ def test_fp8_decode_refuses_before_launch():
     assert call(ws_bytes=ws - 1) == s4kv.S4KV_ERR_WORKSPACE
     for i in range(8):
         assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG
+
+
+def test_probe_refuses_before_launch():
+    lib, P, fake = _raw_calls()
+    assert lib.s4kv_probe_read(None, 1 << 20, fake, 1, 1, 1, None) == s4kv.S4KV_ERR_INVALID_ARG
+    assert lib.s4kv_probe_read(fake, 1 << 20, None, 1, 1, 1, None) == s4kv.S4KV_ERR_INVALID_ARG
+    assert lib.s4kv_probe_read(fake, 4095, fake, 1, 1, 1, None) == s4kv.S4KV_ERR_INVALID_ARG
+    assert lib.s4kv_probe_read(fake, 1 << 20, fake, 0, 1, 1, None) == s4kv.S4KV_ERR_INVALID_ARG
+    assert lib.s4kv_probe_read(fake, 1 << 20, fake, 1, 0, 1, None) == s4kv.S4KV_ERR_INVALID_ARG
