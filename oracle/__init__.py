@@ -34,7 +34,7 @@ against closed forms, special cases, brute force or library routines.
 
 from .quant import QMAX, quantize_groups, dequantize, flush_pages, dequantize_pages
 from .cache import PAGE, sequence_cache, dequantized_sequence
-from .attention import decode_attention, decode_attention_batch
+from .attention import decode_attention, decode_attention_batch, multiquery_attention
 
 __all__ = [
     "QMAX",
@@ -47,4 +47,5 @@ __all__ = [
     "dequantized_sequence",
     "decode_attention",
     "decode_attention_batch",
+    "multiquery_attention",
 ]

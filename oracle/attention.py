@@ -13,6 +13,13 @@ Readings taken here:
 
 The oracle evaluates this in float64 over the fp32 dequantized cache, the
 plain definition with no blocking, splitting or reordering.
+
+Several query tokens per sequence (the prefill side of the two inference
+phases, named on the polaris7.io signal page, "Verwandte Marktsignale &
+Trends", entry on KV caching; also the verify step of speculative decoding):
+the new tokens are already in the cache, the last T of its ctx positions, and
+token t (position ctx - T + t) attends causally to positions 0 .. ctx - T + t
+(reading: causal attention with the new tokens at the end of the cache).
 """
 
 import math
@@ -54,3 +61,19 @@ def decode_attention_batch(q16, seq_khat, seq_vhat, sm_scale=None):
     """:func:`decode_attention` for each sequence; lists of per-sequence caches."""
     return [decode_attention(q16[b], seq_khat[b], seq_vhat[b], sm_scale)
             for b in range(len(seq_khat))]
+
+
+def multiquery_attention(q16, khat, vhat, sm_scale=None):
+    """Causal attention of the last T cache positions' queries.
+
+    ``q16``: [T, Hq, D] queries of the tokens at positions ctx - T .. ctx - 1;
+    ``khat``/``vhat``: [ctx, Hkv, D]. Token t sees positions 0 .. ctx - T + t.
+    Returns float64 [T, Hq, D].
+    """
+    q = np.asarray(q16)
+    ctx = np.asarray(khat).shape[0]
+    t_new = q.shape[0]
+    if not 1 <= t_new <= ctx:
+        raise ValueError("need 1 <= T <= ctx")
+    return np.stack([decode_attention(q[t], khat[:ctx - t_new + t + 1], vhat[:ctx - t_new + t + 1],
+                                      sm_scale) for t in range(t_new)])
