@@ -10,9 +10,10 @@ Headline workload: Llama-3.1-8B-shaped decode, 32 layers, 32 query / 8 KV
 heads, head_dim 128, batch 128, contexts U[2048, 8192], page 16.
 Secondary (same JSON line): Llama-3-70B-shaped decode, 80 layers, 64/8 heads,
 batch 16, 32768-token contexts, with the bulk prefill quantize of those
-contexts timed separately; and the same decode call over this library's
-fp16 (control) and FP8 E4M3 caches against the int4 call, on one layer of the
-headline workload.
+contexts timed separately; the same decode call over this library's fp16
+(control) and FP8 E4M3 caches against the int4 call, on one layer of the
+headline workload; and multi-query attention (4 new tokens per sequence, the
+speculative-verify step) against the decode call on that layer.
 
 Two ceilings frame the decode call's rate: a copy (torch, read + write) and
 the library's read probe (s4kv_probe_read: random 4 KB chunks through the
@@ -348,6 +349,68 @@ def format_comparison(wl, calls=20, warmup=3):
     return out
 
 
+def multiquery_leg(wl, max_q=4, calls=20, warmup=3):
+    """Multi-query attention (speculative verify: max_q new tokens per
+    sequence, already appended) against the one-token decode call, on layer 0
+    of the workload's int4 cache: `calls` calls of each, interleaved, HIP-event
+    medians."""
+    import torch
+    from int4_kivi_quantized_amd import Shape
+    from int4_kivi_quantized_amd.cache import LayerCache
+
+    ctx = W.context_lengths(wl)
+    plan = W.plan_pages(wl, ctx)
+    shape = Shape(wl.batch, wl.hq, wl.hkv, plan.num_pages, plan.max_pages)
+    bt = torch.from_numpy(plan.block_table).cuda()
+    mult = W.k_channel_multipliers(wl, 0)
+    cache = LayerCache(shape)
+    ks, vs = [], []
+    for b in range(wl.batch):
+        k, v = W.sequence_kv(wl, 0, b, int(ctx[b]), "cuda", mult)
+        ks.append(k)
+        vs.append(v)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32), device="cuda")
+    cache.append(torch.cat(ks).contiguous(), torch.cat(vs).contiguous(), cu,
+                 torch.zeros(wl.batch, dtype=torch.int32, device="cuda"), int(ctx.max()), bt)
+    del ks, vs
+    ctx_g = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    max_ctx = int(ctx.max())
+    q1 = W.queries(wl, 0, "cuda")
+    t_counts = np.full(wl.batch, max_q)
+    qm = W.normal_fp16((int(t_counts.sum()), wl.hq, wl.head_dim), 4242, "cuda")
+    cu_q = torch.from_numpy(np.concatenate([[0], np.cumsum(t_counts)]).astype(np.int32)).cuda()
+    out1, outm = torch.empty_like(q1), torch.empty_like(qm)
+    run = {"decode": lambda: cache.decode(q1, bt, ctx_g, max_ctx, out=out1),
+           "mq": lambda: cache.attend(qm, cu_q, max_q, bt, ctx_g, max_ctx, out=outm)}
+    for _ in range(warmup):
+        for f in run.values():
+            f()
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls)] for k in run}
+    torch.cuda.synchronize()
+    for i in range(calls):
+        for k, f in run.items():
+            a, b = ev[k][i]
+            a.record()
+            f()
+            b.record()
+    torch.cuda.synchronize()
+    ms = {k: float(np.median([a.elapsed_time(b) for a, b in ev[k]])) for k in run}
+    del cache, qm, outm, out1
+    torch.cuda.empty_cache()
+    mq_b = A.mq_bytes(ctx, t_counts, wl.hq, wl.hkv)
+    return {
+        "workload": f"{wl.name}, layer 0, {max_q} new tokens per sequence (causal)",
+        "calls": calls,
+        "mq_call_ms": round(ms["mq"], 5),
+        "mq_bytes_per_call": mq_b,
+        "mq_gbs": round(mq_b / (ms["mq"] * 1e-3) / 1e9, 2),
+        "mq_query_tokens_per_s": round(int(t_counts.sum()) / (ms["mq"] * 1e-3), 1),
+        "decode_call_ms": round(ms["decode"], 5),
+        "mq_over_decode_time": round(ms["mq"] / ms["decode"], 4),
+    }
+
+
 def load_traffic(digest):
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if not os.path.exists(path):
@@ -456,6 +519,9 @@ def main():
     if not args.no_secondary:
         print("[bench] format comparison (int4 / fp16 / fp8)", file=sys.stderr, flush=True)
         line["format_comparison"] = format_comparison(wl)
+        torch.cuda.empty_cache()
+        print("[bench] multi-query (verify) attention", file=sys.stderr, flush=True)
+        line["multiquery"] = multiquery_leg(wl)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -165,6 +165,48 @@ s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void
                               int32_t max_ctx, float sm_scale, void* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* ---- multi-query attention over the int4 cache ----
+ *
+ * Several new query tokens per sequence attend over the same pages and tail:
+ * the speculative-decoding verify step and small prefill chunks, the prefill
+ * side of the two inference phases (polaris7.io signal page, "Verwandte
+ * Marktsignale & Trends", the entry on KV caching, which names the prefill
+ * and decoding phases). The new tokens' K and V are appended first
+ * (s4kv_quantize_append), so ctx_lens counts them; token t of the T_b new
+ * tokens of sequence b sits at cache position p = ctx_lens[b] - T_b + t and
+ * attends causally:
+ *   O[row][j] = sum_{s <= p} softmax_s(sm_scale * q[row][j] . k_s) v_s,
+ *   row = cu_q[b] + t, KV head of j = j / (Hq/Hkv).
+ * One launch serves every sequence; max_q * (Hq / Hkv) <= 16. */
+
+/* Bytes of device workspace s4kv_paged_attention_mq needs (0 if the shape is
+ * invalid, max_ctx < 1, max_q < 1 or max_q * Hq / Hkv > 16). */
+size_t s4kv_mq_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx, int32_t max_q);
+
+/* Multi-query attention step.
+ * Args (device pointers unless noted):
+ *   q            fp16 [total_q][Hq][128]: the new tokens' queries, sequence by
+ *                sequence.
+ *   cu_q         int32 [B + 1]: sequence b's tokens are rows cu_q[b] ..
+ *                cu_q[b + 1] - 1; cu_q[0] = 0, cu_q[B] = total_q.
+ *   max_q        host int >= every T_b = cu_q[b + 1] - cu_q[b]; sizes the launch.
+ *   total_q      host int, the number of query rows.
+ *   pages, tail_k, tail_v, block_table, ctx_lens, max_ctx, sm_scale  as
+ *                s4kv_paged_decode (ctx_lens includes the new tokens).
+ *   out          fp16 [total_q][Hq][128]; written.
+ *   workspace    device scratch of at least s4kv_mq_workspace_bytes.
+ * Device preconditions: as s4kv_paged_decode, plus 1 <= T_b <= min(max_q,
+ * ctx_lens[b]) and cu_q as above.
+ * Returns S4KV_OK; S4KV_ERR_INVALID_ARG / S4KV_ERR_UNSUPPORTED (max_q *
+ * Hq / Hkv > 16) / S4KV_ERR_WORKSPACE before any launch; S4KV_ERR_HIP if a
+ * launch fails. */
+s4kv_status s4kv_paged_attention_mq(const s4kv_shape* shape, const void* q, const int32_t* cu_q,
+                                    int32_t max_q, int32_t total_q, const void* pages,
+                                    const void* tail_k, const void* tail_v,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* ---- fp16 control path ----
  *
  * The same cache and decode step with K and V kept in fp16 (the format the

@@ -45,6 +45,27 @@ class LayerCache:
                                ctx_lens, max_ctx, sm_scale, out, self.workspace(max_ctx), stream)
         return out
 
+    def mq_workspace(self, max_ctx, max_q):
+        need = s4kv.s4kv_mq_workspace_bytes(self.shape, max_ctx, max_q)
+        if need == 0:
+            raise s4kv.S4KVError(s4kv.S4KV_ERR_UNSUPPORTED, "mq_workspace")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def attend(self, q, cu_q, max_q, block_table, ctx_lens, max_ctx, sm_scale=None, out=None,
+               stream=None):
+        """Multi-query attention of q fp16 [total_q, Hq, 128] (rows of sequence b:
+        cu_q[b] .. cu_q[b+1]-1, the last ones in the cache) over this layer."""
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(self.shape.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        s4kv.s4kv_paged_attention_mq(self.shape, q, cu_q, max_q, self.pages, self.tail_k,
+                                     self.tail_v, block_table, ctx_lens, max_ctx, sm_scale, out,
+                                     self.mq_workspace(max_ctx, max_q), stream)
+        return out
+
     def chunk_view(self):
         """uint8 [num_pages, Hkv, CHUNK_STRIDE] view of the pool."""
         return self.pages.view(self.shape.num_pages, self.shape.num_kv_heads, s4kv.CHUNK_STRIDE)

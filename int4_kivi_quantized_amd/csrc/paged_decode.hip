@@ -321,19 +321,26 @@ __device__ __host__ inline int owner_wave(int64_t u, int64_t U, int W) {
 // (b*Hkv + h, wave) pair, at slot index (b*Hkv + h) + wave.
 constexpr int kSlotStride = kHeadDim + 4;  // 128 outputs, m, l, 2 pad (16-byte rows)
 
-template <int G>
+// G is the number of matrix-core columns one KV head feeds. For decode it is
+// the query group Hq / Hkv. With kMQ (several query tokens per sequence) a
+// column is a (query token, query head) pair: G = max_q * gq columns, column v
+// holds token v / gq and head v % gq of the group, and attends causally: token
+// t of the T_b new tokens of sequence b sits at position ctx_b - T_b + t and
+// sees the cache positions up to it.
+template <int G, bool kMQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ pages,
     const __half* __restrict__ tail_k, const __half* __restrict__ tail_v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
     int32_t* __restrict__ total_units, int2* __restrict__ seg_waves, int32_t B, int32_t max_pages,
-    int32_t hkv, float sm_scale, float* __restrict__ slots) {
+    int32_t hkv, float sm_scale, float* __restrict__ slots, const int32_t* __restrict__ cu_q,
+    int32_t gq, int32_t total_q) {
   constexpr bool kPacked = (G <= 8);    // columns split between the two pages of a pair
   constexpr bool kHiLoCols = (G <= 4);  // and between the hi / lo parts of the output operand
   const int w = blockIdx.x, W = gridDim.x;
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
-  const int hq = hkv * G;
+  const int hq = hkv * (kMQ ? gq : G);
 
   // ---- unit plan ----
   // units(b) = full pages of b plus one for a non-empty tail; (b, h) pairs are
@@ -451,8 +458,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   Cursor prod = start;
   int issued = 0, consumed = 0;
   int pstage = 0, cstage = 0;  // ring slots of the next issue / the next consume
-  auto q_row = [&](int b, int h) {
-    return reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + h * G + head) * kHeadDim);
+  // kMQ: the column's causal limit (cache position) in the current segment
+  int col_lim = 0;
+  auto q_row = [&](int b, int h, int ctx) {
+    if constexpr (kMQ) {
+      // a sequence with fewer new tokens than columns repeats its last token
+      // in the spare columns (their results are not stored)
+      const int q0 = cu_q[b], tb = cu_q[b + 1] - q0;
+      const int t = min(head / gq, max(tb - 1, 0));
+      col_lim = ctx - tb + t;
+      const int64_t row = min(max((int64_t)q0 + t, (int64_t)0), (int64_t)total_q - 1);
+      return reinterpret_cast<const uint8_t*>(q + (row * hq + h * gq + head % gq) * kHeadDim);
+    } else {
+      return reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + h * G + head) * kHeadDim);
+    }
   };
   // Block ids of the pair at the producer cursor, loaded one pair ahead of
   // their use so the scalar-load latency overlaps a whole iteration. A single
@@ -509,7 +528,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // the query of the new (b, h); loading it waits for the ring's DMAs,
     // once per segment
     u4 raw[4];
-    const uint8_t* qr = q_row(b, h);
+    const uint8_t* qr = q_row(b, h, cu.full * kPage + cu.tail);
 #pragma unroll
     for (int m = 0; m < 4; ++m) raw[m] = ld16(qr + 2 * (32 * m + 8 * g));
 #pragma unroll
@@ -636,7 +655,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // ---- fp16 tail of (cur_b, cur_h): logits and output products on fp16 values;
   // in packed layouts only page-A columns take it
-  auto process_tail = [&](int tail_n) {
+  // tail_pos0: cache position of the tail's first token
+  auto process_tail = [&](int tail_n, int tail_pos0) {
     const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
     const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
     _Float16 (*tv_s)[kHeadDim] = tail_s;
@@ -652,7 +672,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     float mb = kNegInf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lg[i] = (4 * g + i < tail_n && pslot == 0) ? acc[i] * l2s : kNegInf;
+      bool ok = 4 * g + i < tail_n && pslot == 0;
+      if constexpr (kMQ) ok = ok && tail_pos0 + 4 * g + i <= col_lim;
+      lg[i] = ok ? acc[i] * l2s : kNegInf;
       mb = fmaxf(mb, lg[i]);
     }
     mb = rows_max(mb);
@@ -715,7 +737,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     hi = static_cast<_Float16>(__builtin_fmaf(pk, sv, 0.0f));
     lo = static_cast<_Float16>(__builtin_fmaf(pk, sv, -static_cast<float>(hi)));
   };
-  auto process_pair = [&](const uint8_t* st, bool has_b) {
+  // pos0: cache position of page A's first token
+  auto process_pair = [&](const uint8_t* st, bool has_b, int pos0) {
     f4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kPacked) {
       PackedStage r;
@@ -740,6 +763,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       float lg[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) lg[k] = mine[k] * qk_scale + zl;
+      if constexpr (kMQ) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (pos0 + kPage * pslot + 4 * g + k > col_lim) lg[k] = kNegInf;
+      }
       const float mb = rows_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
       rescale_to(mb);
       const float ms = m_sub();
@@ -811,15 +839,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int k = 0; k < 4; ++k) {
         lgA[k] = accA[k] * qk_scale + zA * l2s;
         lgB[k] = accB[k] * qk_scale + zlB;
+        if constexpr (kMQ) {
+          if (pos0 + 4 * g + k > col_lim) lgA[k] = kNegInf;
+          if (pos0 + kPage + 4 * g + k > col_lim) lgB[k] = kNegInf;
+        }
         mb = fmaxf(mb, fmaxf(lgA[k], lgB[k]));
       }
       mb = rows_max(mb);
       rescale_to(mb);
+      // with causal masks a column can still have seen no token (m_run = -inf)
+      const float msw = kMQ ? m_sub() : m_run;
       h8 bhi, blo;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float pa = __builtin_amdgcn_exp2f(lgA[k] - m_run);
-        const float pb = __builtin_amdgcn_exp2f(lgB[k] - m_run);
+        const float pa = __builtin_amdgcn_exp2f(lgA[k] - msw);
+        const float pb = __builtin_amdgcn_exp2f(lgB[k] - msw);
         l_part += pa + pb;
         lz_part += pa * static_cast<float>(h_at2(r.zvA, k)) + pb * static_cast<float>(h_at2(r.zvB, k));
         _Float16 h, l;
@@ -848,10 +882,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // 6 x (pairs issued after this one)" outstanding means this pair has landed
   // in LDS; other outstanding operations (query and tail loads,
   // partial-result stores) can only make the wait stricter.
-  auto consume_pair = [&](int np) {
+  auto consume_pair = [&](int np, int pos0) {
     wait_pages_after<kDmaPerStage, kStages - 1>(issued - consumed - 1);
     compiler_fence();
-    process_pair(stage_s[cstage], np == 2);
+    process_pair(stage_s[cstage], np == 2, pos0);
     if (++cstage == kStages) cstage = 0;
     compiler_fence();
     ++consumed;
@@ -865,12 +899,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // the segment's pages, then its tail if the range reaches it
     int np = entry_pages(cons);
     while (np > 0) {
-      consume_pair(np);
+      consume_pair(np, cons.unit * kPage);
       advance(cons, np);
       np = (cons.u < u1 && cons.b == cur_b && cons.h == cur_h) ? entry_pages(cons) : -1;
     }
     if (np == 0) {
-      process_tail(cons.tail);
+      process_tail(cons.tail, cons.full * kPage);
       advance(cons, 1);
     }
     end_segment();
@@ -884,11 +918,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // max over the slots s. The block is R slot groups x (G heads x 32 output
 // quads): each thread merges every R-th slot of its quad online, then the R
 // partial merges of a quad combine through LDS.
+// With cu_q (several query tokens per sequence) the G columns of a slot are
+// (token, head) pairs, column jj = token jj / gq, head jj % gq; columns past
+// the sequence's token count are merged but not stored.
 constexpr int kReduceThreads = 1024;
 __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
     const float* __restrict__ slots, const int32_t* __restrict__ total_units,
     const int2* __restrict__ seg_waves, const int32_t* __restrict__ ctx_lens, int32_t max_pages,
-    int32_t hkv, int32_t G, int32_t W, __half* __restrict__ out) {
+    int32_t hkv, int32_t G, int32_t W, __half* __restrict__ out, const int32_t* __restrict__ cu_q,
+    int32_t gq, int32_t total_q) {
   __shared__ float red_m[kReduceThreads], red_l[kReduceThreads];
   __shared__ f4 red_o[kReduceThreads];
   const int h = blockIdx.x, b = blockIdx.y;
@@ -897,14 +935,22 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   const int t = threadIdx.x;
   const int combo = t % C, r = t / C;
   const int jj = combo >> 5, d0 = 4 * (combo & 31);
-  const int hq = hkv * G;
-  __half* o = out + ((int64_t)b * hq + h * G + jj) * kHeadDim + d0;
+  __half* o;
+  bool store = true;
+  if (cu_q != nullptr) {
+    const int q0 = cu_q[b], tq = jj / gq;
+    // rows outside [0, total_q) are never written, whatever cu_q holds
+    store = tq < cu_q[b + 1] - q0 && q0 >= 0 && (int64_t)q0 + tq < total_q;
+    o = out + (((int64_t)q0 + tq) * hkv * gq + h * gq + jj % gq) * kHeadDim + d0;
+  } else {
+    o = out + ((int64_t)b * hkv * G + h * G + jj) * kHeadDim + d0;
+  }
   const int64_t bh = (int64_t)b * hkv + h;
   const int n = units_of(ctx_lens[b], max_pages);
   const int64_t U = total_units[0];
   const int2 ws = seg_waves[bh];
   if (n <= 0 || U <= 0) {
-    if (r == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    if (r == 0 && store) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
     return;
   }
   float M = kNegInf, L = 0.f;
@@ -942,6 +988,7 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
       M = Mn;
     }
   }
+  if (!store) return;
   const float inv = 1.0f / L;
   __half2 lo = __floats2half2_rn(acc[0] * inv, acc[1] * inv);
   __half2 hi = __floats2half2_rn(acc[2] * inv, acc[3] * inv);
@@ -951,17 +998,38 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   *reinterpret_cast<uint2*>(o) = pk;
 }
 
-template <int G>
+template <int G, bool kMQ>
 hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages,
                     const void* tail_k, const void* tail_v, const int32_t* block_table,
                     const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves, float sm_scale,
-                    float* slots, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(W), dim3(64), 0, stream,
+                    float* slots, const int32_t* cu_q, int32_t gq, int32_t total_q,
+                    hipStream_t stream) {
+  hipLaunchKernelGGL((decode_stream_kernel<G, kMQ>), dim3(W), dim3(64), 0, stream,
                      static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
                      static_cast<const __half*>(tail_k), static_cast<const __half*>(tail_v),
                      block_table, ctx_lens, total_units, seg_waves, s.num_seqs, s.max_pages_per_seq,
-                     s.num_kv_heads, sm_scale, slots);
+                     s.num_kv_heads, sm_scale, slots, cu_q, gq, total_q);
   return hipGetLastError();
+}
+
+// one instantiation per column count 1..16
+template <bool kMQ>
+hipError_t launch_columns(int G, const s4kv_shape& s, int W, const void* q, const void* pages,
+                          const void* tail_k, const void* tail_v, const int32_t* block_table,
+                          const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves,
+                          float sm_scale, float* slots, const int32_t* cu_q, int32_t gq,
+                          int32_t total_q, hipStream_t stream) {
+  switch (G) {
+#define S4KV_CASE(g)                                                                             \
+  case g:                                                                                        \
+    return launch_g<g, kMQ>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, total_units,  \
+                            seg_waves, sm_scale, slots, cu_q, gq, total_q, stream);
+    S4KV_CASE(1) S4KV_CASE(2) S4KV_CASE(3) S4KV_CASE(4) S4KV_CASE(5) S4KV_CASE(6) S4KV_CASE(7)
+    S4KV_CASE(8) S4KV_CASE(9) S4KV_CASE(10) S4KV_CASE(11) S4KV_CASE(12) S4KV_CASE(13)
+    S4KV_CASE(14) S4KV_CASE(15) S4KV_CASE(16)
+#undef S4KV_CASE
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -998,13 +1066,14 @@ SplitWorkspace split_workspace(const s4kv_shape& s, void* workspace) {
   return w;
 }
 
-hipError_t launch_split_merge(const s4kv_shape& s, int W, int32_t max_ctx, const SplitWorkspace& ws,
-                              const int32_t* ctx_lens, void* out, hipStream_t stream) {
+namespace {
+hipError_t launch_merge(const s4kv_shape& s, int W, int32_t max_ctx, const SplitWorkspace& ws,
+                        const int32_t* ctx_lens, void* out, int G, const int32_t* cu_q, int32_t gq,
+                        int32_t total_q, hipStream_t stream) {
   // Slot groups per (sequence, head): about the number of waves that share a
   // (b, h) when every context is max_ctx long (W waves over B * Hkv * pages
   // units), rounded up to a power of two and capped by the block size. This
   // only sizes the launch; any count of sharing waves is merged correctly.
-  const int G = s.num_q_heads / s.num_kv_heads;
   const int C = 32 * G;
   const int64_t per_bh = ((int64_t)max_ctx + kPage - 1) / kPage;
   const int64_t units = (int64_t)s.num_seqs * s.num_kv_heads * per_bh;
@@ -1013,14 +1082,27 @@ hipError_t launch_split_merge(const s4kv_shape& s, int W, int32_t max_ctx, const
   while (R < share && 2 * R * C <= kReduceThreads) R *= 2;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads, s.num_seqs), dim3(C * R), 0,
                      stream, ws.slots, ws.total_units, reinterpret_cast<const int2*>(ws.seg_waves), ctx_lens, s.max_pages_per_seq,
-                     s.num_kv_heads, G, W, static_cast<__half*>(out));
+                     s.num_kv_heads, G, W, static_cast<__half*>(out), cu_q, gq, total_q);
   return hipGetLastError();
+}
+size_t workspace_for_columns(const s4kv_shape& s, int columns) {
+  const size_t nslots = (size_t)s.num_seqs * s.num_kv_heads + kMaxWaves;
+  return kHeaderBytes + seg_bytes(s) + nslots * columns * kSlotStride * sizeof(float);
+}
+}  // namespace
+
+hipError_t launch_split_merge(const s4kv_shape& s, int W, int32_t max_ctx, const SplitWorkspace& ws,
+                              const int32_t* ctx_lens, void* out, hipStream_t stream) {
+  const int G = s.num_q_heads / s.num_kv_heads;
+  return launch_merge(s, W, max_ctx, ws, ctx_lens, out, G, nullptr, G, s.num_seqs, stream);
 }
 
 size_t workspace_bytes(const s4kv_shape& s) {
-  const size_t nslots = (size_t)s.num_seqs * s.num_kv_heads + kMaxWaves;
-  const int G = s.num_q_heads / s.num_kv_heads;
-  return kHeaderBytes + seg_bytes(s) + nslots * G * kSlotStride * sizeof(float);
+  return workspace_for_columns(s, s.num_q_heads / s.num_kv_heads);
+}
+
+size_t mq_workspace_bytes(const s4kv_shape& s, int32_t max_q) {
+  return workspace_for_columns(s, max_q * (s.num_q_heads / s.num_kv_heads));
 }
 
 hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* pages,
@@ -1031,18 +1113,27 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
   const SplitWorkspace ws = split_workspace(s, workspace);
   const int W = resident_waves();
   const int G = s.num_q_heads / s.num_kv_heads;
-  hipError_t e = hipSuccess;
-  switch (G) {
-#define S4KV_CASE(g) \
-  case g: e = launch_g<g>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, ws.total_units, reinterpret_cast<int2*>(ws.seg_waves), sm_scale, ws.slots, stream); break;
-    S4KV_CASE(1) S4KV_CASE(2) S4KV_CASE(3) S4KV_CASE(4) S4KV_CASE(5) S4KV_CASE(6) S4KV_CASE(7)
-    S4KV_CASE(8) S4KV_CASE(9) S4KV_CASE(10) S4KV_CASE(11) S4KV_CASE(12) S4KV_CASE(13)
-    S4KV_CASE(14) S4KV_CASE(15) S4KV_CASE(16)
-#undef S4KV_CASE
-    default: return hipErrorInvalidValue;
-  }
+  const hipError_t e = launch_columns<false>(G, s, W, q, pages, tail_k, tail_v, block_table, ctx_lens,
+                                             ws.total_units, reinterpret_cast<int2*>(ws.seg_waves),
+                                             sm_scale, ws.slots, nullptr, G, s.num_seqs, stream);
   if (e != hipSuccess) return e;
   return launch_split_merge(s, W, max_ctx, ws, ctx_lens, out, stream);
+}
+
+hipError_t launch_paged_mq(const s4kv_shape& s, const void* q, const int32_t* cu_q, int32_t max_q,
+                           int32_t total_q, const void* pages, const void* tail_k, const void* tail_v,
+                           const int32_t* block_table, const int32_t* ctx_lens, int32_t max_ctx,
+                           float sm_scale, void* out, void* workspace, hipStream_t stream) {
+  const SplitWorkspace ws = split_workspace(s, workspace);
+  const int W = resident_waves();
+  const int gq = s.num_q_heads / s.num_kv_heads;
+  const int columns = max_q * gq;
+  const hipError_t e = launch_columns<true>(columns, s, W, q, pages, tail_k, tail_v, block_table,
+                                            ctx_lens, ws.total_units,
+                                            reinterpret_cast<int2*>(ws.seg_waves), sm_scale, ws.slots,
+                                            cu_q, gq, total_q, stream);
+  if (e != hipSuccess) return e;
+  return launch_merge(s, W, max_ctx, ws, ctx_lens, out, columns, cu_q, gq, total_q, stream);
 }
 
 }  // namespace s4kv

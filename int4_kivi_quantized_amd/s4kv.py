@@ -111,6 +111,11 @@ def load():
     lib.s4kv_fp8_paged_decode.argtypes = [SP, P, P, P, P, I32, ctypes.c_float, P, P, P, P,
                                           ctypes.c_size_t, P]
     lib.s4kv_fp8_paged_decode.restype = ctypes.c_int
+    lib.s4kv_mq_workspace_bytes.argtypes = [SP, I32, I32]
+    lib.s4kv_mq_workspace_bytes.restype = ctypes.c_size_t
+    lib.s4kv_paged_attention_mq.argtypes = [SP, P, P, I32, I32, P, P, P, P, P, I32, ctypes.c_float,
+                                            P, P, ctypes.c_size_t, P]
+    lib.s4kv_paged_attention_mq.restype = ctypes.c_int
     lib.s4kv_probe_read.argtypes = [P, ctypes.c_size_t, P, I32, I32, I32, P]
     lib.s4kv_probe_read.restype = ctypes.c_int
     _lib = lib
@@ -122,6 +127,7 @@ EXPORTED = (
     "s4kv_quantize_append", "s4kv_decode_workspace_bytes", "s4kv_paged_decode",
     "s4kv_fp16_pool_bytes", "s4kv_fp16_append", "s4kv_fp16_paged_decode",
     "s4kv_fp8_pool_bytes", "s4kv_fp8_append", "s4kv_fp8_paged_decode",
+    "s4kv_mq_workspace_bytes", "s4kv_paged_attention_mq",
     "s4kv_probe_read",
 )
 
@@ -197,6 +203,25 @@ def s4kv_paged_decode(shape, q, pages, tail_k, tail_v, block_table, ctx_lens, ma
         int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "s4kv_paged_decode")
+
+
+def s4kv_mq_workspace_bytes(shape, max_ctx, max_q):
+    return load().s4kv_mq_workspace_bytes(ctypes.byref(shape.c()), int(max_ctx), int(max_q))
+
+
+def s4kv_paged_attention_mq(shape, q, cu_q, max_q, pages, tail_k, tail_v, block_table, ctx_lens,
+                            max_ctx, sm_scale, out, workspace, stream=None):
+    """Multi-query attention: out fp16 [total_q, Hq, 128] from q fp16 [total_q, Hq, 128], the
+    rows of sequence b being cu_q[b] .. cu_q[b+1]-1 (int32 [B+1]); see s4kv.h."""
+    import torch
+    st = load().s4kv_paged_attention_mq(
+        ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(cu_q, torch.int32, "cu_q"),
+        int(max_q), int(q.shape[0]), _ptr(pages, torch.uint8, "pages"),
+        _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_lens, torch.int32, "ctx_lens"),
+        int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "s4kv_paged_attention_mq")
 
 
 def s4kv_fp16_pool_bytes(shape):

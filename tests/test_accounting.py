@@ -77,3 +77,11 @@ def test_fp8_decode_bytes():
     assert kv == A.fp16_kv_bytes(1, 8, 128, int(ctx.sum()), bytes_per_elem=1)
     # half the fp16 payload
     assert 2 * kv == A.fp16_kv_bytes(1, 8, 128, int(ctx.sum()))
+
+
+def test_mq_bytes():
+    # one token per sequence: the decode bytes plus the B + 1 query-row offsets
+    ctx = np.array([37, 100])
+    assert A.mq_bytes(ctx, [1, 1], 12, 3) == A.decode_bytes(ctx, 12, 3) + 4 * 3
+    # each extra token adds its Q row and O row (fp16, Hq x 128)
+    assert A.mq_bytes(ctx, [4, 2], 12, 3) - A.mq_bytes(ctx, [1, 1], 12, 3) == 4 * 4 * 12 * 128

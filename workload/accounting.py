@@ -65,6 +65,18 @@ def fp16_decode_bytes(ctx_lens, num_q_heads, kv_heads):
                + 2 * (2 * b * num_q_heads * HEAD_DIM))
 
 
+def mq_bytes(ctx_lens, t_counts, num_q_heads, kv_heads):
+    """Algorithmic HBM bytes of one multi-query attention launch (one layer):
+    the decode bytes with Q read and O written for every new token, plus the
+    query-row offsets (B + 1 int32)."""
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    t = np.asarray(t_counts, dtype=np.int64)
+    b = len(ctx)
+    full = ctx // PAGE
+    return int(cache_bytes(ctx, kv_heads) + 4 * full.sum() + 4 * b + 4 * (b + 1)
+               + 2 * (2 * int(t.sum()) * num_q_heads * HEAD_DIM))
+
+
 FP8_TOKEN_BYTES = 2 * HEAD_DIM                                                # K + V, 256
 
 
