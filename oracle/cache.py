@@ -20,10 +20,11 @@ from .quant import flush_pages, dequantize_pages
 PAGE = 16
 
 
-def sequence_cache(k16, v16):
+def sequence_cache(k16, v16, bits=4):
     """Cache state of one sequence.
 
     ``k16``, ``v16``: float16 ``[ctx, Hkv, D]``, the token stream so far.
+    ``bits``: code width of the full pages (4, or 2 for the 2-bit variant).
 
     Returns a dict:
       ``full``  number of int4 pages (ctx // 16),
@@ -38,7 +39,7 @@ def sequence_cache(k16, v16):
     full = ctx // PAGE
     kp = k16[: full * PAGE].reshape(full, PAGE, hkv, d).transpose(0, 2, 1, 3)
     vp = v16[: full * PAGE].reshape(full, PAGE, hkv, d).transpose(0, 2, 1, 3)
-    pages = flush_pages(np.ascontiguousarray(kp), np.ascontiguousarray(vp))
+    pages = flush_pages(np.ascontiguousarray(kp), np.ascontiguousarray(vp), bits)
     return {
         "full": full,
         "pages": pages,

@@ -21,6 +21,11 @@ its reason in the design notes) are:
 6. a negative-zero scale or zero point is stored as +0.
 
 Dequantization is x_hat = code * scale + zero in fp32.
+
+The same rule with 2-bit codes (scale = (max - min) / 3, codes 0..3) is the
+KIVI variant the KV-cache explainer cites (analyticslegends.ai, "Quellen",
+entry 17: KIVI, a tuning-free asymmetric 2-bit quantization of the KV cache):
+``bits=2`` replaces 15 by 3 in readings 2 and 4, everything else unchanged.
 """
 
 import numpy as np
@@ -30,20 +35,29 @@ _F32 = np.float32
 _F16 = np.float16
 
 
-def quantize_groups(x16, axis=-1):
+def qmax_of(bits):
+    """Largest code of a ``bits``-wide unsigned code (4 -> 15, 2 -> 3)."""
+    if bits not in (2, 4):
+        raise ValueError("codes are 4 or 2 bits wide")
+    return (1 << bits) - 1
+
+
+def quantize_groups(x16, axis=-1, bits=4):
     """Quantize fp16 groups lying along ``axis``.
 
     Parameters
     ----------
     x16 : ndarray of float16. Each 1-D slice along ``axis`` is one group.
     axis : the group axis.
+    bits : code width, 4 (codes 0..15) or 2 (codes 0..3).
 
     Returns
     -------
-    codes : uint8 array, same shape as ``x16``, values in 0..15.
+    codes : uint8 array, same shape as ``x16``, values in 0..qmax.
     scale : float16 array, ``x16`` with ``axis`` removed.
     zero  : float16 array, same shape as ``scale``.
     """
+    qmax = qmax_of(bits)
     x16 = np.asarray(x16)
     if x16.dtype != _F16:
         raise TypeError("quantize_groups expects float16 input")
@@ -51,8 +65,8 @@ def quantize_groups(x16, axis=-1):
     # Reading 1: the group extremes are fp16 values, compared exactly.
     mn = xg.min(axis=-1)
     mx = xg.max(axis=-1)
-    # Reading 2 and 4: fp32 range, fp32 division by 15, round to fp16 (RNE).
-    s32 = (mx.astype(_F32) - mn.astype(_F32)) / _F32(QMAX)
+    # Reading 2 and 4: fp32 range, fp32 division by qmax, round to fp16 (RNE).
+    s32 = (mx.astype(_F32) - mn.astype(_F32)) / _F32(qmax)
     s16 = s32.astype(_F16)
     z16 = mn.astype(_F16)
     # Reading 6: canonical +0.
@@ -63,7 +77,7 @@ def quantize_groups(x16, axis=-1):
     zero_scale = s16 == 0
     denom = np.where(zero_scale, _F32(1.0), s16.astype(_F32)).astype(_F32)
     t = (xg.astype(_F32) - z16.astype(_F32)[..., None]) / denom[..., None]
-    q = np.clip(np.rint(t), 0, QMAX)
+    q = np.clip(np.rint(t), 0, qmax)
     # Reading 5: a zero scale gives all-zero codes.
     q = np.where(zero_scale[..., None], _F32(0.0), q)
     codes = np.moveaxis(q.astype(np.uint8), -1, axis)
@@ -79,7 +93,7 @@ def dequantize(codes, scale, zero, axis=-1):
     return np.moveaxis(x.astype(_F32), -1, axis)
 
 
-def flush_pages(k16, v16):
+def flush_pages(k16, v16, bits=4):
     """Quantize full 16-token pages.
 
     ``k16``, ``v16``: float16 arrays ``[..., 16, D]`` (token, channel) holding
@@ -97,8 +111,8 @@ def flush_pages(k16, v16):
     v16 = np.asarray(v16)
     if k16.shape != v16.shape or k16.shape[-2] != 16:
         raise ValueError("pages must be [..., 16, D] for K and V alike")
-    ck, sk, zk = quantize_groups(k16, axis=-2)
-    cv, sv, zv = quantize_groups(v16, axis=-1)
+    ck, sk, zk = quantize_groups(k16, axis=-2, bits=bits)
+    cv, sv, zv = quantize_groups(v16, axis=-1, bits=bits)
     return {"ck": ck, "sk": sk, "zk": zk, "cv": cv, "sv": sv, "zv": zv}
 
 

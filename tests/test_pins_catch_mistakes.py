@@ -48,12 +48,12 @@ def _some_pin_fails():
     return False
 
 
-def _swap(orig, x16, axis):
+def _swap(orig, x16, axis, bits=4):
     # K grouped per token instead of per channel
     if axis == -2:
-        c, s, z = orig(x16, axis=-1)
+        c, s, z = orig(x16, axis=-1, bits=bits)
         return c, s[..., :1].repeat(x16.shape[-1], -1)[..., : x16.shape[-1]], z[..., :1].repeat(x16.shape[-1], -1)
-    return orig(x16, axis=axis)
+    return orig(x16, axis=axis, bits=bits)
 
 
 def _mutants():
@@ -61,8 +61,8 @@ def _mutants():
     orig_dq = oquant.dequantize
     orig_cache = ocache.sequence_cache
 
-    def keep_neg_zero(x16, axis=-1):
-        c, s, z = orig_q(x16, axis)
+    def keep_neg_zero(x16, axis=-1, bits=4):
+        c, s, z = orig_q(x16, axis, bits)
         z = np.where(z == 0, np.float16(-0.0), z).astype(np.float16)
         return c, s, z
 
@@ -95,8 +95,9 @@ def _mutants():
         "round_half_up": ("np", oquant, _NpProxy(rint=lambda t: np.floor(t + 0.5))),
         "no_clamp": ("np", oquant, _NpProxy(clip=lambda a, lo, hi: a)),
         "round_toward_zero": ("np", oquant, _NpProxy(rint=np.trunc)),
-        "scale_over_16": ("QMAX", oquant, 16),
-        "k_grouped_per_token": ("quantize_groups", oquant, lambda x, axis=-1: _swap(orig_q, x, axis)),
+        "scale_over_16": ("qmax_of", oquant, lambda bits=4: 16 if bits == 4 else 4),
+        "k_grouped_per_token": ("quantize_groups", oquant,
+                                lambda x, axis=-1, bits=4: _swap(orig_q, x, axis, bits)),
         "keep_negative_zero": ("quantize_groups", oquant, keep_neg_zero),
         "dequant_drops_zero": ("dequantize", oquant, drop_zero_point),
         "tail_off_by_one": ("sequence_cache", ocache, tail_off_by_one),
