@@ -10,8 +10,8 @@ Headline workload: Llama-3.1-8B-shaped decode, 32 layers, 32 query / 8 KV
 heads, head_dim 128, batch 128, contexts U[2048, 8192], page 16.
 Secondary (same JSON line): Llama-3-70B-shaped decode, 80 layers, 64/8 heads,
 batch 16, 32768-token contexts, with the bulk prefill quantize of those
-contexts timed separately; the same decode call over this library's fp16
-(control) and FP8 E4M3 caches against the int4 call, on one layer of the
+contexts timed separately; the same decode call over this library's 2-bit
+KIVI, fp16 (control) and FP8 E4M3 caches against the int4 call, on one layer of the
 headline workload; and multi-query attention (4 new tokens per sequence, the
 speculative-verify step) against the decode call on that layer.
 
@@ -281,16 +281,17 @@ def read_ceiling(reps=10):
 
 
 def format_comparison(wl, calls=20, warmup=3):
-    """The same decode over the three caches of this library on one layer of
+    """The same decode over the four caches of this library on one layer of
     the workload: layer 0's cache built as int4 (s4kv_quantize_append), as
-    fp16 (s4kv_fp16_append, the control path) and as FP8 E4M3
+    2-bit KIVI (s4kv_kivi2_quantize_append), as fp16 (s4kv_fp16_append, the
+    control path) and as FP8 E4M3
     (s4kv_fp8_append, per-KV-head scales calibrated on sequence 0: its
     largest magnitude over 448); then `calls` decode calls of each,
     interleaved, each timed with HIP events on the call's stream; medians are
     reported, with each format's algorithmic bytes per call."""
     import torch
     from int4_kivi_quantized_amd import Shape
-    from int4_kivi_quantized_amd.cache import Fp8LayerCache, Fp16LayerCache, LayerCache
+    from int4_kivi_quantized_amd.cache import Fp8LayerCache, Fp16LayerCache, Kivi2LayerCache, LayerCache
 
     ctx = W.context_lengths(wl)
     plan = W.plan_pages(wl, ctx)
@@ -313,8 +314,8 @@ def format_comparison(wl, calls=20, warmup=3):
     max_ctx = int(ctx.max())
     # all caches resident, calls interleaved, so no measurement sees a
     # different allocation history or clock state than the others
-    caches = {"int4": LayerCache(shape), "fp16": Fp16LayerCache(shape),
-              "fp8": Fp8LayerCache(shape, k_scale.cpu(), v_scale.cpu())}
+    caches = {"int4": LayerCache(shape), "kivi2": Kivi2LayerCache(shape),
+              "fp16": Fp16LayerCache(shape), "fp8": Fp8LayerCache(shape, k_scale.cpu(), v_scale.cpu())}
     outs = {}
     for name, cache in caches.items():
         cache.append(k_all, v_all, cu, sl, int(ctx.max()), bt)
@@ -337,15 +338,17 @@ def format_comparison(wl, calls=20, warmup=3):
     del caches, outs
     torch.cuda.empty_cache()
     nbytes = {"int4": A.decode_bytes(ctx, wl.hq, wl.hkv),
+              "kivi2": A.decode_bytes(ctx, wl.hq, wl.hkv, A.K2_CHUNK_BYTES),
               "fp16": A.fp16_decode_bytes(ctx, wl.hq, wl.hkv),
               "fp8": A.fp8_decode_bytes(ctx, wl.hq, wl.hkv)}
     out = {"workload": f"{wl.name}, layer 0 (no append)", "calls": calls}
-    for name in ("int4", "fp16", "fp8"):
+    for name in ("int4", "kivi2", "fp16", "fp8"):
         gbs = nbytes[name] / (res[name] * 1e-3) / 1e9
         out[name] = {"call_ms": round(res[name], 5), "bytes_per_call": nbytes[name],
                      "gbs": round(gbs, 2), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4)}
     out["int4_speedup_over_fp16"] = round(res["fp16"] / res["int4"], 4)
     out["int4_speedup_over_fp8"] = round(res["fp8"] / res["int4"], 4)
+    out["kivi2_speedup_over_int4"] = round(res["int4"] / res["kivi2"], 4)
     return out
 
 
@@ -517,7 +520,7 @@ def main():
             "prefill_ms_per_layer": round(r2["prefill_ms_per_layer"], 4),
         }
     if not args.no_secondary:
-        print("[bench] format comparison (int4 / fp16 / fp8)", file=sys.stderr, flush=True)
+        print("[bench] format comparison (int4 / kivi2 / fp16 / fp8)", file=sys.stderr, flush=True)
         line["format_comparison"] = format_comparison(wl)
         torch.cuda.empty_cache()
         print("[bench] multi-query (verify) attention", file=sys.stderr, flush=True)

@@ -165,6 +165,50 @@ s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void
                               int32_t max_ctx, float sm_scale, void* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* ---- 2-bit KIVI pages ----
+ *
+ * The same cache with 2-bit codes: the KIVI paper the KV-cache explainer
+ * cites (analyticslegends.ai, "Quellen", entry 17) quantizes the cache
+ * asymmetrically to 2 bits, KEY per channel and VALUE per token. Same
+ * grouping, tail, rounding rule and entry-point conventions as the int4
+ * calls, with scale = (max - min) / 3 and codes 0..3.
+ *
+ * 2-bit page format: pool uint8 [num_pages][num_kv_heads][1664]; each chunk
+ * holds 1600 bytes of data, then 64 bytes of padding (written as zero):
+ *   [   0, 512) K codes   [ 512,1024) V codes
+ *   [1024,1280) K scale fp16[128] (per channel)   [1280,1536) K zero fp16[128]
+ *   [1536,1568) V scale fp16[16] (per token)      [1568,1600) V zero fp16[16]
+ * Code blocks: lane L = 16 g + c owns bytes 8 L .. 8 L + 7, two little-endian
+ * 32-bit words dd = 0, 1, each code 2 bits wide:
+ *   K (token c): word dd holds channel 32 m + 8 g + i for m = 2 dd + mm
+ *     (mm = 0, 1) and i = 0..7, at bit 8 mm + 2 (i >> 1) + 16 (i & 1);
+ *   V (channel offset c): word dd holds channel 16 (4 dd + s) + c of token
+ *     4 g + k for s = 0..3 and k = 0..3, at bit 4 s + 2 (k >> 1) + 16 (k & 1).
+ * Full pages cost 100 bytes per token per KV head (5.12x denser than fp16). */
+#define S4KV_K2_CHUNK_BYTES 1600  /* data bytes of one (page, KV head) chunk */
+#define S4KV_K2_CHUNK_STRIDE 1664 /* chunk pitch in the pool (13 x 128 B) */
+
+/* Bytes of one layer's 2-bit pool: num_pages * num_kv_heads * 1664; 0 if the
+ * shape is invalid. The tails and the decode workspace are the int4 ones
+ * (s4kv_tail_bytes, s4kv_decode_workspace_bytes). */
+size_t s4kv_kivi2_pool_bytes(const s4kv_shape* shape);
+
+/* s4kv_quantize_append with 2-bit codes: same arguments, statuses and device
+ * preconditions; pages is the 2-bit pool. */
+s4kv_status s4kv_kivi2_quantize_append(const s4kv_shape* shape, const void* k, const void* v,
+                                       const int32_t* cu_new, const int32_t* slot,
+                                       int32_t max_new, const int32_t* block_table, void* pages,
+                                       void* tail_k, void* tail_v, void* stream);
+
+/* s4kv_paged_decode over 2-bit pages: same arguments, statuses, workspace and
+ * device preconditions; k_t, v_t of full pages are code * scale + zero of the
+ * 2-bit codes. */
+s4kv_status s4kv_kivi2_paged_decode(const s4kv_shape* shape, const void* q, const void* pages,
+                                    const void* tail_k, const void* tail_v,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* ---- multi-query attention over the int4 cache ----
  *
  * Several new query tokens per sequence attend over the same pages and tail:

@@ -77,6 +77,38 @@ class LayerCache:
         return self.tail_k.view(*dims), self.tail_v.view(*dims)
 
 
+class Kivi2LayerCache(LayerCache):
+    """One layer's 2-bit KIVI cache: the int4 cache's tails and workspace with a
+    2-bit page pool and the s4kv_kivi2_* entry points."""
+
+    def __init__(self, shape, device="cuda"):
+        super().__init__(shape, device)
+        self.pages = torch.zeros(s4kv.s4kv_kivi2_pool_bytes(shape), dtype=torch.uint8,
+                                 device=self.device)
+
+    def append(self, k, v, cu_new, slot, max_new, block_table, stream=None):
+        s4kv.s4kv_kivi2_quantize_append(self.shape, k, v, cu_new, slot, max_new, block_table,
+                                        self.pages, self.tail_k, self.tail_v, stream)
+
+    def decode(self, q, block_table, ctx_lens, max_ctx, sm_scale=None, out=None, stream=None):
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(self.shape.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        s4kv.s4kv_kivi2_paged_decode(self.shape, q, self.pages, self.tail_k, self.tail_v,
+                                     block_table, ctx_lens, max_ctx, sm_scale, out,
+                                     self.workspace(max_ctx), stream)
+        return out
+
+    def attend(self, *args, **kwargs):
+        raise NotImplementedError("multi-query attention runs over int4 pages only")
+
+    def chunk_view(self):
+        """uint8 [num_pages, Hkv, 1664] view of the pool."""
+        return self.pages.view(self.shape.num_pages, self.shape.num_kv_heads,
+                               s4kv.K2_CHUNK_STRIDE)
+
+
 class Fp16LayerCache:
     """One layer's fp16 paged cache (the control path): pool and workspace."""
 

@@ -97,6 +97,47 @@ s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void
   return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
 }
 
+size_t s4kv_kivi2_pool_bytes(const s4kv_shape* shape) {
+  if (check_shape(shape) != S4KV_OK) return 0;
+  return (size_t)shape->num_pages * shape->num_kv_heads * S4KV_K2_CHUNK_STRIDE;
+}
+
+s4kv_status s4kv_kivi2_quantize_append(const s4kv_shape* shape, const void* k, const void* v,
+                                       const int32_t* cu_new, const int32_t* slot,
+                                       int32_t max_new, const int32_t* block_table, void* pages,
+                                       void* tail_k, void* tail_v, void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (max_new < 0) return S4KV_ERR_INVALID_ARG;
+  if (!k || !v || !cu_new || !slot || !block_table || !pages || !tail_k || !tail_v)
+    return S4KV_ERR_INVALID_ARG;
+  if (max_new == 0) return S4KV_OK;
+  if ((int64_t)max_new > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
+    return S4KV_ERR_INVALID_ARG;
+  const hipError_t e = s4kv::launch_quantize_append(*shape, k, v, cu_new, slot, max_new,
+                                                    block_table, pages, tail_k, tail_v,
+                                                    static_cast<hipStream_t>(stream), 2);
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
+s4kv_status s4kv_kivi2_paged_decode(const s4kv_shape* shape, const void* q, const void* pages,
+                                    const void* tail_k, const void* tail_v,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
+    return S4KV_ERR_INVALID_ARG;
+  if (!q || !pages || !tail_k || !tail_v || !block_table || !ctx_lens || !out || !workspace)
+    return S4KV_ERR_INVALID_ARG;
+  if (workspace_bytes < s4kv::workspace_bytes(*shape)) return S4KV_ERR_WORKSPACE;
+  const hipError_t e = s4kv::launch_paged_decode(*shape, q, pages, tail_k, tail_v, block_table,
+                                                 ctx_lens, max_ctx, sm_scale, out, workspace,
+                                                 static_cast<hipStream_t>(stream), 2);
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
 size_t s4kv_mq_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx, int32_t max_q) {
   if (check_shape(shape) != S4KV_OK || max_ctx < 1 || max_q < 1) return 0;
   if ((int64_t)max_q * (shape->num_q_heads / shape->num_kv_heads) > S4KV_MAX_GROUP) return 0;

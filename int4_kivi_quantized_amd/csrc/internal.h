@@ -22,6 +22,16 @@ constexpr int kOffKZero = 2304;
 constexpr int kOffVScale = 2560;
 constexpr int kOffVZero = 2592;
 
+// 2-bit KIVI pages (see s4kv.h, "2-bit KIVI pages").
+constexpr int kK2ChunkBytes = S4KV_K2_CHUNK_BYTES;
+constexpr int kK2ChunkStride = S4KV_K2_CHUNK_STRIDE;
+constexpr int kOff2KCodes = 0;
+constexpr int kOff2VCodes = 512;
+constexpr int kOff2KScale = 1024;
+constexpr int kOff2KZero = 1280;
+constexpr int kOff2VScale = 1536;
+constexpr int kOff2VZero = 1568;
+
 // Decode workspace: the total unit count, the waves sharing each (sequence, head)
 // and the per-(sequence, head, wave) partial results. The int4 and fp16 decode
 // paths share it and the merge kernel.
@@ -46,10 +56,11 @@ constexpr int kMaxWaves = 4096;
 hipError_t launch_split_merge(const s4kv_shape& s, int W, int32_t max_ctx, const SplitWorkspace& ws,
                               const int32_t* ctx_lens, void* out, hipStream_t stream);
 
+// bits: 4 (int4 pages) or 2 (2-bit KIVI pages)
 hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void* v,
                                   const int32_t* cu_new, const int32_t* slot, int32_t max_new,
                                   const int32_t* block_table, void* pages, void* tail_k,
-                                  void* tail_v, hipStream_t stream);
+                                  void* tail_v, hipStream_t stream, int bits = 4);
 
 // Multi-query attention over the int4 cache: up to max_q query tokens per
 // sequence (max_q * Hq / Hkv <= 16), causal within the sequence.
@@ -59,11 +70,12 @@ hipError_t launch_paged_mq(const s4kv_shape& s, const void* q, const int32_t* cu
                            const int32_t* block_table, const int32_t* ctx_lens, int32_t max_ctx,
                            float sm_scale, void* out, void* workspace, hipStream_t stream);
 
+// bits: 4 (int4 pages) or 2 (2-bit KIVI pages)
 hipError_t launch_paged_decode(const s4kv_shape& s, const void* q,
                                const void* pages, const void* tail_k, const void* tail_v,
                                const int32_t* block_table, const int32_t* ctx_lens,
                                int32_t max_ctx, float sm_scale, void* out, void* workspace,
-                               hipStream_t stream);
+                               hipStream_t stream, int bits = 4);
 
 // Dense paged caches (dense_decode.hip): fp16 control path and FP8 E4M3.
 constexpr int kF16ChunkHalves = 2 * S4KV_PAGE_SIZE * S4KV_HEAD_DIM;  // K block, then V^T block

@@ -45,6 +45,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace s4kv {
@@ -64,9 +66,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // is c * p * s * 2^-24.
 constexpr float kQkUnscale = 268435456.0f;  // 2^28
 constexpr float kPvUnscale = 16777216.0f;   // 2^24
-// A V scale is at most (65504 + 65504) / 15 < 2^13.1 and fp16 holds values
-// below 2^16, so p * sV stays finite while p <= 2^2.
-constexpr float kLazyRescale = 2.0f;
 
 __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 
@@ -95,8 +94,47 @@ __device__ inline void v_operands(uint32_t wa, uint32_t wb, h8& even, h8& odd) {
   odd = as_h8(o);
 }
 
+// 2-bit codes (pages of the 2-bit format): a mask keeps two codes per dword,
+// one in each fp16 half, at bits 0-1 (x 2^-24) or 2-3 (x 2^-22). K operand m
+// from dword m / 2 of the lane's 8 bytes, shifted by 8 for odd m: elements
+// 0,1 / 4,5 carry 2^-24 and 2,3 / 6,7 carry 2^-22, the int4 slot pattern with
+// a ratio of 4 instead of 16.
+constexpr uint32_t kM2Lo = 0x00030003u, kM2Hi = 0x000C000Cu;
+__device__ inline h8 k_operand2(uint32_t w, int odd) {
+  const uint32_t x = odd ? (w >> 8) : w;
+  const uint32_t x4 = x >> 4;
+  u4 v;
+  v[0] = x & kM2Lo;
+  v[1] = x & kM2Hi;
+  v[2] = x4 & kM2Lo;
+  v[3] = x4 & kM2Hi;
+  return as_h8(v);
+}
+// V tiles 2m and 2m+1 of a pair: tile u lives in dword u / 4 of each page at
+// shift 4 (u % 4); elements 0..3 from page A, 4..7 from page B.
+__device__ inline void v_operands2(uint32_t wa, uint32_t wb, int m, h8& even, h8& odd) {
+  const int sh = 8 * (m & 1);
+  const uint32_t ea = wa >> sh, eb = wb >> sh, oa = ea >> 4, ob = eb >> 4;
+  u4 e, o;
+  e[0] = ea & kM2Lo; e[1] = ea & kM2Hi; e[2] = eb & kM2Lo; e[3] = eb & kM2Hi;
+  o[0] = oa & kM2Lo; o[1] = oa & kM2Hi; o[2] = ob & kM2Lo; o[3] = ob & kM2Hi;
+  even = as_h8(e);
+  odd = as_h8(o);
+}
+
 __device__ inline u4 ld16(const uint8_t* p) { return *reinterpret_cast<const u4*>(p); }
 __device__ inline u2 ld8(const uint8_t* p) { return *reinterpret_cast<const u2*>(p); }
+
+// Operands of a pair by code width (u4: a lane's 16 int4 bytes, u2: its 8
+// 2-bit bytes).
+__device__ inline h8 k_op(const u4& kc, int m) { return k_operand(kc[m]); }
+__device__ inline h8 k_op(const u2& kc, int m) { return k_operand2(kc[m >> 1], m & 1); }
+__device__ inline void v_ops(const u4& a, const u4& b, int m, h8& even, h8& odd) {
+  v_operands(a[m], b[m], even, odd);
+}
+__device__ inline void v_ops(const u2& a, const u2& b, int m, h8& even, h8& odd) {
+  v_operands2(a[m >> 1], b[m >> 1], m, even, odd);
+}
 
 __device__ inline _Float16 h_at(u4 v, int i) { return __builtin_bit_cast(h8, v)[i]; }
 __device__ inline _Float16 h_at2(u2 v, int i) {
@@ -175,12 +213,40 @@ __device__ inline void zero_terms(const h8 (&qh)[4], const u4 (&z)[4], float& ta
 //   [2048,3072) V codes page A     [3072,4096) V codes page B
 //   [4096,4608) K scale+zero A     [4608,5120) K scale+zero B
 //   [5120,5184) V scale+zero A     [5184,5248) V scale+zero B
-constexpr int kStageBytes = 5248;
-// One stage: the wave reads it into registers and refills it at once, so the
-// next pair loads while this one is computed. Deeper rings measured slower
-// (more bytes in flight per wave only queue longer).
-constexpr int kStages = 1;
-constexpr int kDmaPerStage = 6;     // DMA instructions issued per stage
+//
+// With 2-bit pages a stage is:
+//   [   0, 512) K codes page A     [ 512,1024) K codes page B
+//   [1024,1536) V codes page A     [1536,2048) V codes page B
+//   [2048,2560) K scale+zero A     [2560,3072) K scale+zero B
+//   [3072,3136) V scale+zero A     [3136,3200) V scale+zero B
+// kStages (per code width): the wave reads a stage into registers and
+// refills it at once, so the next pairs load while this one is computed.
+
+// Per code width: stage geometry, DMA count, chunk pitch, and the factors of
+// the second slot group (query side, probability side); see k_operand /
+// k_operand2. kLazy bounds p: the largest V scale is (65504 + 65504) / qmax
+// (< 2^13.1 for int4, < 2^15.42 for 2 bits), and p * sV must stay below the
+// fp16 maximum 65504 (2^15.999).
+template <int kBits>
+struct PairFmt;
+template <>
+struct PairFmt<4> {
+  static constexpr int kStageBytes = 5248, kDmaPerStage = 6, kKMeta = 4096, kVMeta = 5120;
+  static constexpr int kStride = kChunkStride;
+  // one stage: deeper rings measured slower (more bytes in flight per wave
+  // only queue longer at this rate)
+  static constexpr int kStages = 1;
+  static constexpr float kQSlot23 = 0.00390625f, kPSlot23 = 0.0625f;  // 2^-8, 1/16
+  static constexpr float kLazy = 2.0f;
+};
+template <>
+struct PairFmt<2> {
+  static constexpr int kStageBytes = 3200, kDmaPerStage = 4, kKMeta = 2048, kVMeta = 3072;
+  static constexpr int kStride = kK2ChunkStride;
+  static constexpr int kStages = 1;
+  static constexpr float kQSlot23 = 0.015625f, kPSlot23 = 0.25f;  // 2^-6, 1/4
+  static constexpr float kLazy = 0.5f;
+};
 
 // Every cache byte is read once: the loads carry the non-temporal policy (nt),
 // which streams them past the caches; on MI355X a pure read of 4 KB chunks
@@ -304,6 +370,92 @@ __device__ inline void read_stage_wide(uint32_t base, int lane, int g, int zrow,
   read_kvec(base + 512 * zrow + 256 + 16 * g, r.ze);
 }
 
+// The same stages for 2-bit pages: a lane's codes are 8 bytes per page.
+struct PackedStage2 {
+  u2 kcA, kcB, vcA, vcB;
+  u2 sv, zv;
+  u4 sc[4];
+  u4 ze[4];
+};
+__device__ inline void read_stage_packed2(uint32_t base, int lane, int g, int page, int zrow,
+                                          PackedStage2& r) {
+  const uint32_t a_lane = base + 8 * lane;
+  const uint32_t a_v = base + 64 * page + 8 * g;
+  const uint32_t a_k = base + 512 * page + 16 * g;
+  const uint32_t a_z = base + 512 * zrow + 16 * g;
+  __asm__ __volatile__(
+      "ds_read_b64 %0, %14\n\t"
+      "ds_read_b64 %1, %14 offset:512\n\t"
+      "ds_read_b64 %2, %14 offset:1024\n\t"
+      "ds_read_b64 %3, %14 offset:1536\n\t"
+      "ds_read_b64 %4, %15 offset:3072\n\t"
+      "ds_read_b64 %5, %15 offset:3104\n\t"
+      "ds_read_b128 %6, %16 offset:2048\n\t"
+      "ds_read_b128 %7, %16 offset:2112\n\t"
+      "ds_read_b128 %8, %16 offset:2176\n\t"
+      "ds_read_b128 %9, %16 offset:2240\n\t"
+      "ds_read_b128 %10, %17 offset:2304\n\t"
+      "ds_read_b128 %11, %17 offset:2368\n\t"
+      "ds_read_b128 %12, %17 offset:2432\n\t"
+      "ds_read_b128 %13, %17 offset:2496\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.kcA), "=&v"(r.kcB), "=&v"(r.vcA), "=&v"(r.vcB), "=&v"(r.sv), "=&v"(r.zv),
+        "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3]), "=&v"(r.ze[0]),
+        "=&v"(r.ze[1]), "=&v"(r.ze[2]), "=&v"(r.ze[3])
+      : "v"(a_lane), "v"(a_v), "v"(a_k), "v"(a_z)
+      : "memory");
+}
+// K scale of one page, or (at byte offset 256 past it) K zero, 2-bit stage
+__device__ inline void read_kvec2(uint32_t addr, u4 (&v)[4]) {
+  __asm__ __volatile__(
+      "ds_read_b128 %0, %4 offset:2048\n\t"
+      "ds_read_b128 %1, %4 offset:2112\n\t"
+      "ds_read_b128 %2, %4 offset:2176\n\t"
+      "ds_read_b128 %3, %4 offset:2240\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(addr)
+      : "memory");
+}
+struct WideStage2 {
+  u2 kcA, kcB, vcA, vcB;
+  u2 svA, zvA, svB, zvB;
+  u4 scA[4], scB[4], ze[4];
+};
+__device__ inline void read_stage_wide2(uint32_t base, int lane, int g, int zrow, WideStage2& r) {
+  const uint32_t a_lane = base + 8 * lane;
+  const uint32_t a_v = base + 8 * g;
+  __asm__ __volatile__(
+      "ds_read_b64 %0, %8\n\t"
+      "ds_read_b64 %1, %8 offset:512\n\t"
+      "ds_read_b64 %2, %8 offset:1024\n\t"
+      "ds_read_b64 %3, %8 offset:1536\n\t"
+      "ds_read_b64 %4, %9 offset:3072\n\t"
+      "ds_read_b64 %5, %9 offset:3104\n\t"
+      "ds_read_b64 %6, %9 offset:3136\n\t"
+      "ds_read_b64 %7, %9 offset:3168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.kcA), "=&v"(r.kcB), "=&v"(r.vcA), "=&v"(r.vcB), "=&v"(r.svA), "=&v"(r.zvA),
+        "=&v"(r.svB), "=&v"(r.zvB)
+      : "v"(a_lane), "v"(a_v)
+      : "memory");
+  read_kvec2(base + 16 * g, r.scA);
+  read_kvec2(base + 512 + 16 * g, r.scB);
+  read_kvec2(base + 512 * zrow + 256 + 16 * g, r.ze);
+}
+__device__ inline void read_packed(uint32_t base, int lane, int g, int page, int zrow, PackedStage& r) {
+  read_stage_packed(base, lane, g, page, zrow, r);
+}
+__device__ inline void read_packed(uint32_t base, int lane, int g, int page, int zrow, PackedStage2& r) {
+  read_stage_packed2(base, lane, g, page, zrow, r);
+}
+__device__ inline void read_wide(uint32_t base, int lane, int g, int zrow, WideStage& r) {
+  read_stage_wide(base, lane, g, zrow, r);
+}
+__device__ inline void read_wide(uint32_t base, int lane, int g, int zrow, WideStage2& r) {
+  read_stage_wide2(base, lane, g, zrow, r);
+}
+
 // units of a sequence: its full pages, plus one for a non-empty tail
 __device__ inline int units_of(int ctx, int max_pages) {
   ctx = min(ctx, max_pages * kPage);
@@ -327,7 +479,7 @@ constexpr int kSlotStride = kHeadDim + 4;  // 128 outputs, m, l, 2 pad (16-byte 
 // holds token v / gq and head v % gq of the group, and attends causally: token
 // t of the T_b new tokens of sequence b sits at position ctx_b - T_b + t and
 // sees the cache positions up to it.
-template <int G, bool kMQ>
+template <int G, bool kMQ, int kBits>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ pages,
     const __half* __restrict__ tail_k, const __half* __restrict__ tail_v,
@@ -341,6 +493,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
   const int hq = hkv * (kMQ ? gq : G);
+  using PF = PairFmt<kBits>;
+  constexpr int kStages = PF::kStages;
+  using PStage = std::conditional_t<kBits == 4, PackedStage, PackedStage2>;
+  using WStage = std::conditional_t<kBits == 4, WideStage, WideStage2>;
 
   // ---- unit plan ----
   // units(b) = full pages of b plus one for a non-empty tail; (b, h) pairs are
@@ -453,7 +609,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   // ---- DMA ring ----
-  __shared__ __align__(16) uint8_t stage_s[kStages][kStageBytes];
+  __shared__ __align__(16) uint8_t stage_s[kStages][PF::kStageBytes];
   __shared__ __align__(16) _Float16 tail_s[kPage][kHeadDim];  // fp16 tail V, one (b, h) at a time
   Cursor prod = start;
   int issued = 0, consumed = 0;
@@ -495,16 +651,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int np = entry_pages(prod);
     const int idA = nid_a, idB = nid_b;
     // chunk index id * Hkv + h < num_pages * Hkv fits in 32 bits
-    const uint8_t* chA = pages + static_cast<uint64_t>(static_cast<uint32_t>(idA * hkv + prod.h)) * kChunkStride;
-    const uint8_t* chB = pages + static_cast<uint64_t>(static_cast<uint32_t>(idB * hkv + prod.h)) * kChunkStride;
+    const uint8_t* chA = pages + static_cast<uint64_t>(static_cast<uint32_t>(idA * hkv + prod.h)) * PF::kStride;
+    const uint8_t* chB = pages + static_cast<uint64_t>(static_cast<uint32_t>(idB * hkv + prod.h)) * PF::kStride;
     uint8_t* st = stage_s[pstage];
     if (++pstage == kStages) pstage = 0;
-    dma16(chA + kOffKCodes + 16 * lane, st + 0);
-    dma16(chB + kOffKCodes + 16 * lane, st + 1024);
-    dma16(chA + kOffVCodes + 16 * lane, st + 2048);
-    dma16(chB + kOffVCodes + 16 * lane, st + 3072);
-    dma16((lane < 32 ? chA : chB) + kOffKScale + 16 * (lane & 31), st + 4096);
-    if (lane < 8) dma16((lane < 4 ? chA : chB) + kOffVScale + 16 * (lane & 3), st + 5120);
+    if constexpr (kBits == 4) {
+      dma16(chA + kOffKCodes + 16 * lane, st + 0);
+      dma16(chB + kOffKCodes + 16 * lane, st + 1024);
+      dma16(chA + kOffVCodes + 16 * lane, st + 2048);
+      dma16(chB + kOffVCodes + 16 * lane, st + 3072);
+      dma16((lane < 32 ? chA : chB) + kOffKScale + 16 * (lane & 31), st + 4096);
+      if (lane < 8) dma16((lane < 4 ? chA : chB) + kOffVScale + 16 * (lane & 3), st + 5120);
+    } else {
+      // each 512-byte block: lanes 0..31 from page A, 32..63 from page B
+      const uint8_t* half = (lane < 32 ? chA : chB) + 16 * (lane & 31);
+      dma16(half + kOff2KCodes, st + 0);
+      dma16(half + kOff2VCodes, st + 1024);
+      dma16(half + kOff2KScale, st + 2048);
+      if (lane < 8) dma16((lane < 4 ? chA : chB) + kOff2VScale + 16 * (lane & 3), st + 3072);
+    }
     ++issued;
     advance(prod, np);
     prefetch_ids();
@@ -539,7 +704,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       qh[m] = v;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        qc[m][i] = static_cast<_Float16>(static_cast<float>(v[i]) * (((i & 2) == 0) ? 0.0625f : 0.00390625f));
+        qc[m][i] = static_cast<_Float16>(static_cast<float>(v[i]) * (((i & 2) == 0) ? 0.0625f : PF::kQSlot23));
     }
     m_run = kNegInf;
     l_part = 0.f;
@@ -635,11 +800,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   // The reference max of a column moves only when a logit passes it by more
-  // than kLazyRescale (log2 units), so most pages skip rescaling the
-  // accumulators; a probability is then at most 2^kLazyRescale, which keeps
+  // than PF::kLazy (log2 units), so most pages skip rescaling the
+  // accumulators; a probability is then at most 2^PF::kLazy, which keeps
   // p * sV inside the fp16 range for every fp16 V scale.
   auto rescale_to = [&](float mb) {
-    const bool up = mb > m_run + kLazyRescale;
+    const bool up = mb > m_run + PF::kLazy;
     if (__any(up)) {
       const float mnew = up ? mb : m_run;
       const float alpha = (mnew == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
@@ -733,7 +898,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
   // fp16 (hi, lo) parts of x = p * s for output slot k (slots 2,3,6,7 carry 1/16)
   auto ps_split = [&](float pk, _Float16 s, int k, _Float16& hi, _Float16& lo) {
-    const float sv = static_cast<float>(s) * (((k & 2) == 0) ? 1.0f : 0.0625f);
+    const float sv = static_cast<float>(s) * (((k & 2) == 0) ? 1.0f : PF::kPSlot23);
     hi = static_cast<_Float16>(__builtin_fmaf(pk, sv, 0.0f));
     lo = static_cast<_Float16>(__builtin_fmaf(pk, sv, -static_cast<float>(hi)));
   };
@@ -741,16 +906,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   auto process_pair = [&](const uint8_t* st, bool has_b, int pos0) {
     f4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kPacked) {
-      PackedStage r;
-      read_stage_packed(lds_addr(st), lane, g, pslot, zrow, r);
+      PStage r;
+      read_packed(lds_addr(st), lane, g, pslot, zrow, r);
       refill();
       // ---- logits of this column's page (K scale of that page in the operand) ----
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
         qs_split(qc[m], r.sc[m], hi, lo);
-        const h8 ka = k_operand(r.kcA[m]);
-        const h8 kb = k_operand(r.kcB[m]);
+        const h8 ka = k_op(r.kcA, m);
+        const h8 kb = k_op(r.kcB, m);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
         accB = mfma(kb, hi, accB);
@@ -798,7 +963,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           h8 ve, vo;
-          v_operands(r.vcA[m], r.vcB[m], ve, vo);
+          v_ops(r.vcA, r.vcB, m, ve, vo);
           o[2 * m] = mfma(ve, b, o[2 * m]);
           o[2 * m + 1] = mfma(vo, b, o[2 * m + 1]);
         }
@@ -807,7 +972,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           h8 ve, vo;
-          v_operands(r.vcA[m], r.vcB[m], ve, vo);
+          v_ops(r.vcA, r.vcB, m, ve, vo);
           o[2 * m] = mfma(ve, bh, o[2 * m]);
           o[2 * m] = mfma(ve, bl, o[2 * m]);
           o[2 * m + 1] = mfma(vo, bh, o[2 * m + 1]);
@@ -815,18 +980,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
       }
     } else {
-      WideStage r;
-      read_stage_wide(lds_addr(st), lane, g, zrow, r);
+      WStage r;
+      read_wide(lds_addr(st), lane, g, zrow, r);
       refill();
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 hi, lo;
         qs_split(qc[m], r.scA[m], hi, lo);
-        const h8 ka = k_operand(r.kcA[m]);
+        const h8 ka = k_op(r.kcA, m);
         accA = mfma(ka, hi, accA);
         accA = mfma(ka, lo, accA);
         qs_split(qc[m], r.scB[m], hi, lo);
-        const h8 kb = k_operand(r.kcB[m]);
+        const h8 kb = k_op(r.kcB, m);
         accB = mfma(kb, hi, accB);
         accB = mfma(kb, lo, accB);
       }
@@ -867,7 +1032,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         h8 ve, vo;
-        v_operands(r.vcA[m], r.vcB[m], ve, vo);
+        v_ops(r.vcA, r.vcB, m, ve, vo);
         o[2 * m] = mfma(ve, bhi, o[2 * m]);
         o[2 * m] = mfma(ve, blo, o[2 * m]);
         o[2 * m + 1] = mfma(vo, bhi, o[2 * m + 1]);
@@ -883,7 +1048,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // in LDS; other outstanding operations (query and tail loads,
   // partial-result stores) can only make the wait stricter.
   auto consume_pair = [&](int np, int pos0) {
-    wait_pages_after<kDmaPerStage, kStages - 1>(issued - consumed - 1);
+    wait_pages_after<PF::kDmaPerStage, kStages - 1>(issued - consumed - 1);
     compiler_fence();
     process_pair(stage_s[cstage], np == 2, pos0);
     if (++cstage == kStages) cstage = 0;
@@ -998,13 +1163,13 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   *reinterpret_cast<uint2*>(o) = pk;
 }
 
-template <int G, bool kMQ>
+template <int G, bool kMQ, int kBits>
 hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages,
                     const void* tail_k, const void* tail_v, const int32_t* block_table,
                     const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves, float sm_scale,
                     float* slots, const int32_t* cu_q, int32_t gq, int32_t total_q,
                     hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<G, kMQ>), dim3(W), dim3(64), 0, stream,
+  hipLaunchKernelGGL((decode_stream_kernel<G, kMQ, kBits>), dim3(W), dim3(64), 0, stream,
                      static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
                      static_cast<const __half*>(tail_k), static_cast<const __half*>(tail_v),
                      block_table, ctx_lens, total_units, seg_waves, s.num_seqs, s.max_pages_per_seq,
@@ -1013,7 +1178,7 @@ hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages
 }
 
 // one instantiation per column count 1..16
-template <bool kMQ>
+template <bool kMQ, int kBits>
 hipError_t launch_columns(int G, const s4kv_shape& s, int W, const void* q, const void* pages,
                           const void* tail_k, const void* tail_v, const int32_t* block_table,
                           const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves,
@@ -1022,8 +1187,9 @@ hipError_t launch_columns(int G, const s4kv_shape& s, int W, const void* q, cons
   switch (G) {
 #define S4KV_CASE(g)                                                                             \
   case g:                                                                                        \
-    return launch_g<g, kMQ>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, total_units,  \
-                            seg_waves, sm_scale, slots, cu_q, gq, total_q, stream);
+    return launch_g<g, kMQ, kBits>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens,       \
+                                   total_units,                                                  \
+                                   seg_waves, sm_scale, slots, cu_q, gq, total_q, stream);
     S4KV_CASE(1) S4KV_CASE(2) S4KV_CASE(3) S4KV_CASE(4) S4KV_CASE(5) S4KV_CASE(6) S4KV_CASE(7)
     S4KV_CASE(8) S4KV_CASE(9) S4KV_CASE(10) S4KV_CASE(11) S4KV_CASE(12) S4KV_CASE(13)
     S4KV_CASE(14) S4KV_CASE(15) S4KV_CASE(16)
@@ -1109,13 +1275,18 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
                                const void* tail_k, const void* tail_v,
                                const int32_t* block_table, const int32_t* ctx_lens,
                                int32_t max_ctx, float sm_scale, void* out, void* workspace,
-                               hipStream_t stream) {
+                               hipStream_t stream, int bits) {
   const SplitWorkspace ws = split_workspace(s, workspace);
   const int W = resident_waves();
   const int G = s.num_q_heads / s.num_kv_heads;
-  const hipError_t e = launch_columns<false>(G, s, W, q, pages, tail_k, tail_v, block_table, ctx_lens,
-                                             ws.total_units, reinterpret_cast<int2*>(ws.seg_waves),
-                                             sm_scale, ws.slots, nullptr, G, s.num_seqs, stream);
+  const hipError_t e =
+      (bits == 2)
+          ? launch_columns<false, 2>(G, s, W, q, pages, tail_k, tail_v, block_table, ctx_lens,
+                                     ws.total_units, reinterpret_cast<int2*>(ws.seg_waves), sm_scale,
+                                     ws.slots, nullptr, G, s.num_seqs, stream)
+          : launch_columns<false, 4>(G, s, W, q, pages, tail_k, tail_v, block_table, ctx_lens,
+                                     ws.total_units, reinterpret_cast<int2*>(ws.seg_waves), sm_scale,
+                                     ws.slots, nullptr, G, s.num_seqs, stream);
   if (e != hipSuccess) return e;
   return launch_split_merge(s, W, max_ctx, ws, ctx_lens, out, stream);
 }
@@ -1128,7 +1299,7 @@ hipError_t launch_paged_mq(const s4kv_shape& s, const void* q, const int32_t* cu
   const int W = resident_waves();
   const int gq = s.num_q_heads / s.num_kv_heads;
   const int columns = max_q * gq;
-  const hipError_t e = launch_columns<true>(columns, s, W, q, pages, tail_k, tail_v, block_table,
+  const hipError_t e = launch_columns<true, 4>(columns, s, W, q, pages, tail_k, tail_v, block_table,
                                             ctx_lens, ws.total_units,
                                             reinterpret_cast<int2*>(ws.seg_waves), sm_scale, ws.slots,
                                             cu_q, gq, total_q, stream);

@@ -13,6 +13,11 @@
 // Rounding is fixed so that codes are reproducible bit for bit: IEEE fp32
 // subtract and correctly rounded divide (HIP's default division), round half
 // to even, clamp to [0, 15]; no contraction into fused multiply-adds.
+//
+// The same kernel, instantiated for 2-bit codes, fills the 2-bit KIVI pages
+// (the KIVI paper cited by the KV-cache explainer, analyticslegends.ai,
+// "Quellen", entry 17): scale (max - min) / 3, codes 0..3, the page layout of
+// s4kv.h's 2-bit section.
 #pragma clang fp contract(off)
 
 #include <hip/hip_fp16.h>
@@ -23,6 +28,24 @@
 namespace s4kv {
 namespace {
 
+// Code width: page geometry and the largest code.
+template <int kBits>
+struct Codes;
+template <>
+struct Codes<4> {
+  static constexpr float kQmax = 15.0f;
+  static constexpr int kStride = kChunkStride, kData = kChunkBytes;
+  static constexpr int kK = kOffKCodes, kV = kOffVCodes, kKs = kOffKScale, kKz = kOffKZero,
+                       kVs = kOffVScale, kVz = kOffVZero;
+};
+template <>
+struct Codes<2> {
+  static constexpr float kQmax = 3.0f;
+  static constexpr int kStride = kK2ChunkStride, kData = kK2ChunkBytes;
+  static constexpr int kK = kOff2KCodes, kV = kOff2VCodes, kKs = kOff2KScale, kKz = kOff2KZero,
+                       kVs = kOff2VScale, kVz = kOff2VZero;
+};
+
 struct GroupQ {
   __half s;
   __half z;
@@ -31,9 +54,10 @@ struct GroupQ {
 };
 
 // Scale/zero of a group from its fp32 min and max (both exact fp16 values).
+template <int kBits>
 __device__ inline GroupQ group_params(float mn, float mx) {
   GroupQ g;
-  const float s32 = (mx - mn) / 15.0f;
+  const float s32 = (mx - mn) / Codes<kBits>::kQmax;
   g.s = __float2half_rn(s32);
   g.z = __float2half_rn(mn);
   g.sf = __half2float(g.s);
@@ -43,10 +67,11 @@ __device__ inline GroupQ group_params(float mn, float mx) {
   return g;
 }
 
+template <int kBits>
 __device__ inline uint32_t code_of(float x, const GroupQ& g) {
   if (g.sf == 0.0f) return 0u;
   float t = rintf((x - g.zf) / g.sf);
-  t = fminf(fmaxf(t, 0.0f), 15.0f);
+  t = fminf(fmaxf(t, 0.0f), Codes<kBits>::kQmax);
   return static_cast<uint32_t>(t);
 }
 
@@ -57,6 +82,7 @@ __device__ inline const __half* token_row(int pos, int start, int64_t in_row0, i
   return in + ((in_row0 + (pos - start)) * hkv + h) * kHeadDim;
 }
 
+template <int kBits>
 __global__ __launch_bounds__(64) void quantize_append_kernel(
     const __half* __restrict__ k, const __half* __restrict__ v, const int32_t* __restrict__ cu_new,
     const int32_t* __restrict__ slot, const int32_t* __restrict__ block_table, int32_t max_pages,
@@ -82,9 +108,10 @@ __global__ __launch_bounds__(64) void quantize_append_kernel(
   __shared__ uint8_t kc[kPage][kHeadDim];
   __shared__ uint8_t vc[kPage][kHeadDim];
 
+  using C = Codes<kBits>;
   if ((p + 1) * kPage <= end) {
     // ---- the page is full: quantize its 16 tokens ----
-    uint8_t* chunk = pages + ((int64_t)block_table[(int64_t)b * max_pages + p] * hkv + h) * kChunkStride;
+    uint8_t* chunk = pages + ((int64_t)block_table[(int64_t)b * max_pages + p] * hkv + h) * C::kStride;
 
     // K: lane owns channels 2*lane, 2*lane+1; groups run over the 16 tokens.
     float k0[kPage], k1[kPage];
@@ -101,15 +128,15 @@ __global__ __launch_bounds__(64) void quantize_append_kernel(
       mn0 = fminf(mn0, k0[t]); mx0 = fmaxf(mx0, k0[t]);
       mn1 = fminf(mn1, k1[t]); mx1 = fmaxf(mx1, k1[t]);
     }
-    const GroupQ g0 = group_params(mn0, mx0);
-    const GroupQ g1 = group_params(mn1, mx1);
+    const GroupQ g0 = group_params<kBits>(mn0, mx0);
+    const GroupQ g1 = group_params<kBits>(mn1, mx1);
 #pragma unroll
     for (int t = 0; t < kPage; ++t) {
-      kc[t][2 * lane] = static_cast<uint8_t>(code_of(k0[t], g0));
-      kc[t][2 * lane + 1] = static_cast<uint8_t>(code_of(k1[t], g1));
+      kc[t][2 * lane] = static_cast<uint8_t>(code_of<kBits>(k0[t], g0));
+      kc[t][2 * lane + 1] = static_cast<uint8_t>(code_of<kBits>(k1[t], g1));
     }
-    reinterpret_cast<__half2*>(chunk + kOffKScale)[lane] = __halves2half2(g0.s, g1.s);
-    reinterpret_cast<__half2*>(chunk + kOffKZero)[lane] = __halves2half2(g0.z, g1.z);
+    reinterpret_cast<__half2*>(chunk + C::kKs)[lane] = __halves2half2(g0.s, g1.s);
+    reinterpret_cast<__half2*>(chunk + C::kKz)[lane] = __halves2half2(g0.z, g1.z);
 
     // V: lane owns token t = lane/4, channels 32*(lane%4) .. +32; groups run
     // over the token's 128 channels (4 lanes per token).
@@ -132,47 +159,91 @@ __global__ __launch_bounds__(64) void quantize_append_kernel(
     for (int i = 1; i < 32; ++i) { vmn = fminf(vmn, vx[i]); vmx = fmaxf(vmx, vx[i]); }
     vmn = fminf(vmn, __shfl_xor(vmn, 1)); vmx = fmaxf(vmx, __shfl_xor(vmx, 1));
     vmn = fminf(vmn, __shfl_xor(vmn, 2)); vmx = fmaxf(vmx, __shfl_xor(vmx, 2));
-    const GroupQ gv = group_params(vmn, vmx);
+    const GroupQ gv = group_params<kBits>(vmn, vmx);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) vc[vt][32 * vu + i] = static_cast<uint8_t>(code_of(vx[i], gv));
+    for (int i = 0; i < 32; ++i) vc[vt][32 * vu + i] = static_cast<uint8_t>(code_of<kBits>(vx[i], gv));
     if (vu == 0) {
-      reinterpret_cast<__half*>(chunk + kOffVScale)[vt] = gv.s;
-      reinterpret_cast<__half*>(chunk + kOffVZero)[vt] = gv.z;
+      reinterpret_cast<__half*>(chunk + C::kVs)[vt] = gv.s;
+      reinterpret_cast<__half*>(chunk + C::kVz)[vt] = gv.z;
     }
-    if (lane < 16) reinterpret_cast<uint32_t*>(chunk + kChunkBytes)[lane] = 0u;
+    // the 64 padding bytes after the data
+    if (lane < 16) reinterpret_cast<uint32_t*>(chunk + C::kData)[lane] = 0u;
     __syncthreads();
 
-    // Pack nibbles in the page order of s4kv.h: lane writes its 16-byte block.
-    {
-      const int t = lane & 15, g = lane >> 4;
-      uint32_t dw[4];
+    if constexpr (kBits == 4) {
+      // Pack nibbles in the page order of s4kv.h: lane writes its 16-byte block.
+      {
+        const int t = lane & 15, g = lane >> 4;
+        uint32_t dw[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint32_t w = 0;
+        for (int m = 0; m < 4; ++m) {
+          uint32_t w = 0;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const int d = 32 * m + 8 * g + 2 * (kk & 3) + (kk >> 2);
-          w |= static_cast<uint32_t>(kc[t][d]) << (4 * kk);
+          for (int kk = 0; kk < 8; ++kk) {
+            const int d = 32 * m + 8 * g + 2 * (kk & 3) + (kk >> 2);
+            w |= static_cast<uint32_t>(kc[t][d]) << (4 * kk);
+          }
+          dw[m] = w;
         }
-        dw[m] = w;
+        reinterpret_cast<uint4*>(chunk + kOffKCodes)[lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
       }
-      reinterpret_cast<uint4*>(chunk + kOffKCodes)[lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
-    }
-    {
-      const int r = lane & 15, g = lane >> 4;
-      uint32_t dw[4];
+      {
+        const int r = lane & 15, g = lane >> 4;
+        uint32_t dw[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint32_t w = 0;
+        for (int m = 0; m < 4; ++m) {
+          uint32_t w = 0;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const int t = 4 * g + 2 * (kk & 1) + (kk >> 2);
-          const int d = 16 * (2 * m + ((kk & 3) >> 1)) + r;
-          w |= static_cast<uint32_t>(vc[t][d]) << (4 * kk);
+          for (int kk = 0; kk < 8; ++kk) {
+            const int t = 4 * g + 2 * (kk & 1) + (kk >> 2);
+            const int d = 16 * (2 * m + ((kk & 3) >> 1)) + r;
+            w |= static_cast<uint32_t>(vc[t][d]) << (4 * kk);
+          }
+          dw[m] = w;
         }
-        dw[m] = w;
+        reinterpret_cast<uint4*>(chunk + kOffVCodes)[lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
       }
-      reinterpret_cast<uint4*>(chunk + kOffVCodes)[lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    } else {
+      // 2-bit codes in the page order of s4kv.h: lane l writes 8 bytes of
+      // each code block. K: lane 16g + t holds token t; dword dd carries
+      // operands m = 2dd, 2dd + 1, element i (channel 32m + 8g + i) at bit
+      // 8 (m & 1) + 2 (i >> 1) + 16 (i & 1).
+      {
+        const int t = lane & 15, g = lane >> 4;
+        uint32_t dw[2];
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int m = 2 * dd + mm;
+              w |= static_cast<uint32_t>(kc[t][32 * m + 8 * g + i]) << (8 * mm + 2 * (i >> 1) + 16 * (i & 1));
+            }
+          dw[dd] = w;
+        }
+        reinterpret_cast<uint2*>(chunk + C::kK)[lane] = make_uint2(dw[0], dw[1]);
+      }
+      // V: lane 16g + r holds channel 16 u + r of tokens 4g .. 4g+3 for the
+      // 8 tiles u; dword dd carries tiles u = 4dd + sub, token 4g + k at bit
+      // 4 sub + 2 (k >> 1) + 16 (k & 1).
+      {
+        const int r = lane & 15, g = lane >> 4;
+        uint32_t dw[2];
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+              w |= static_cast<uint32_t>(vc[4 * g + kk][16 * (4 * dd + sub) + r])
+                   << (4 * sub + 2 * (kk >> 1) + 16 * (kk & 1));
+          dw[dd] = w;
+        }
+        reinterpret_cast<uint2*>(chunk + C::kV)[lane] = make_uint2(dw[0], dw[1]);
+      }
     }
   }
 
@@ -196,11 +267,18 @@ __global__ __launch_bounds__(64) void quantize_append_kernel(
 hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void* v,
                                   const int32_t* cu_new, const int32_t* slot, int32_t max_new,
                                   const int32_t* block_table, void* pages, void* tail_k,
-                                  void* tail_v, hipStream_t stream) {
+                                  void* tail_v, hipStream_t stream, int bits) {
   // pages touched by n tokens starting anywhere inside a page: floor((n+14)/16)+1
   const int slots = (max_new + 14) / kPage + 1;
   dim3 grid(slots, s.num_kv_heads, s.num_seqs);
-  hipLaunchKernelGGL(quantize_append_kernel, grid, dim3(64), 0, stream,
+  if (bits == 2) {
+    hipLaunchKernelGGL(quantize_append_kernel<2>, grid, dim3(64), 0, stream,
+                       static_cast<const __half*>(k), static_cast<const __half*>(v), cu_new, slot,
+                       block_table, s.max_pages_per_seq, static_cast<uint8_t*>(pages),
+                       static_cast<__half*>(tail_k), static_cast<__half*>(tail_v), s.num_kv_heads);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(quantize_append_kernel<4>, grid, dim3(64), 0, stream,
                      static_cast<const __half*>(k), static_cast<const __half*>(v), cu_new, slot,
                      block_table, s.max_pages_per_seq, static_cast<uint8_t*>(pages),
                      static_cast<__half*>(tail_k), static_cast<__half*>(tail_v), s.num_kv_heads);

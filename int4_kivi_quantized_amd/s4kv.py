@@ -22,6 +22,8 @@ CHUNK_STRIDE = 2688
 MAX_GROUP = 16
 F16_CHUNK_BYTES = 8192  # fp16 control pool: K [16][128] then V^T [128][16] per (page, KV head)
 FP8_CHUNK_BYTES = 4096  # FP8 pool: E4M3 K and V per (page, KV head), operand order
+K2_CHUNK_BYTES = 1600   # 2-bit KIVI pool: data bytes per (page, KV head)
+K2_CHUNK_STRIDE = 1664  # and the chunk pitch
 
 S4KV_OK = 0
 S4KV_ERR_INVALID_ARG = 1
@@ -111,6 +113,13 @@ def load():
     lib.s4kv_fp8_paged_decode.argtypes = [SP, P, P, P, P, I32, ctypes.c_float, P, P, P, P,
                                           ctypes.c_size_t, P]
     lib.s4kv_fp8_paged_decode.restype = ctypes.c_int
+    lib.s4kv_kivi2_pool_bytes.argtypes = [SP]
+    lib.s4kv_kivi2_pool_bytes.restype = ctypes.c_size_t
+    lib.s4kv_kivi2_quantize_append.argtypes = [SP, P, P, P, P, I32, P, P, P, P, P]
+    lib.s4kv_kivi2_quantize_append.restype = ctypes.c_int
+    lib.s4kv_kivi2_paged_decode.argtypes = [SP, P, P, P, P, P, P, I32, ctypes.c_float, P, P,
+                                            ctypes.c_size_t, P]
+    lib.s4kv_kivi2_paged_decode.restype = ctypes.c_int
     lib.s4kv_mq_workspace_bytes.argtypes = [SP, I32, I32]
     lib.s4kv_mq_workspace_bytes.restype = ctypes.c_size_t
     lib.s4kv_paged_attention_mq.argtypes = [SP, P, P, I32, I32, P, P, P, P, P, I32, ctypes.c_float,
@@ -128,6 +137,7 @@ EXPORTED = (
     "s4kv_fp16_pool_bytes", "s4kv_fp16_append", "s4kv_fp16_paged_decode",
     "s4kv_fp8_pool_bytes", "s4kv_fp8_append", "s4kv_fp8_paged_decode",
     "s4kv_mq_workspace_bytes", "s4kv_paged_attention_mq",
+    "s4kv_kivi2_pool_bytes", "s4kv_kivi2_quantize_append", "s4kv_kivi2_paged_decode",
     "s4kv_probe_read",
 )
 
@@ -290,3 +300,33 @@ def s4kv_probe_read(pool, chunk_ids, chunks_per_wave, waves, non_temporal=True, 
         _ptr(pool, torch.uint8, "pool"), pool.numel(), _ptr(chunk_ids, torch.int32, "chunk_ids"),
         int(chunks_per_wave), int(waves), 1 if non_temporal else 0, _stream(stream))
     _check(st, "s4kv_probe_read")
+
+
+def s4kv_kivi2_pool_bytes(shape):
+    return load().s4kv_kivi2_pool_bytes(ctypes.byref(shape.c()))
+
+
+def s4kv_kivi2_quantize_append(shape, k, v, cu_new, slot, max_new, block_table, pages, tail_k,
+                               tail_v, stream=None):
+    """s4kv_quantize_append with 2-bit codes into the 2-bit pool; see s4kv.h."""
+    import torch
+    st = load().s4kv_kivi2_quantize_append(
+        ctypes.byref(shape.c()), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
+        _ptr(cu_new, torch.int32, "cu_new"), _ptr(slot, torch.int32, "slot"), int(max_new),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(pages, torch.uint8, "pages"),
+        _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),
+        _stream(stream))
+    _check(st, "s4kv_kivi2_quantize_append")
+
+
+def s4kv_kivi2_paged_decode(shape, q, pages, tail_k, tail_v, block_table, ctx_lens, max_ctx,
+                            sm_scale, out, workspace, stream=None):
+    """s4kv_paged_decode over the 2-bit pool; see s4kv.h."""
+    import torch
+    st = load().s4kv_kivi2_paged_decode(
+        ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(pages, torch.uint8, "pages"),
+        _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_lens, torch.int32, "ctx_lens"),
+        int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "s4kv_kivi2_paged_decode")

@@ -9,7 +9,7 @@ import torch
 import oracle
 import workload as W
 from int4_kivi_quantized_amd import Shape
-from int4_kivi_quantized_amd.cache import Fp8LayerCache, Fp16LayerCache, LayerCache
+from int4_kivi_quantized_amd.cache import Fp8LayerCache, Fp16LayerCache, Kivi2LayerCache, LayerCache
 
 
 def calibrated_fp8_scales(wl, layer=0, mult=None, device="cuda"):
@@ -27,13 +27,14 @@ def calibrated_fp8_scales(wl, layer=0, mult=None, device="cuda"):
 class LayerCase:
     """One layer of a workload: the GPU cache and everything needed to check it.
 
-    kind: "int4" (s4kv_quantize_append / s4kv_paged_decode), "fp16" (the
-    control cache, s4kv_fp16_*) or "fp8" (s4kv_fp8_*, with per-KV-head scales
-    fp8_scales = (k_scale, v_scale); calibrated from sequence 0 by default)."""
+    kind: "int4" (s4kv_quantize_append / s4kv_paged_decode), "kivi2" (2-bit
+    pages, s4kv_kivi2_*), "fp16" (the control cache, s4kv_fp16_*) or "fp8"
+    (s4kv_fp8_*, with per-KV-head scales fp8_scales = (k_scale, v_scale);
+    calibrated from sequence 0 by default)."""
 
     def __init__(self, wl, layer=0, ctx_lens=None, extra_tokens=0, pool_seed_salt=None, kind="int4",
                  fp8_scales=None):
-        assert kind in ("int4", "fp16", "fp8")
+        assert kind in ("int4", "kivi2", "fp16", "fp8")
         self.kind = kind
         self.fp16 = kind == "fp16"
         self.wl = wl
@@ -51,8 +52,11 @@ class LayerCase:
             self.cache = Fp8LayerCache(self.shape, torch.from_numpy(ks), torch.from_numpy(vs))
         elif kind == "fp16":
             self.cache = Fp16LayerCache(self.shape)
+        elif kind == "kivi2":
+            self.cache = Kivi2LayerCache(self.shape)
         else:
             self.cache = LayerCache(self.shape)
+        self.bits = 2 if kind == "kivi2" else 4
         self.block_table = torch.from_numpy(self.plan.block_table).cuda()
         self.ctx_gpu = torch.from_numpy(self.ctx.astype(np.int32)).cuda()
         self.q = W.queries(wl, layer, "cuda")
@@ -81,6 +85,10 @@ class LayerCase:
                 s4kv.s4kv_fp8_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
                                      wl.shared_prefix, bt, self.cache.k_scale, self.cache.v_scale,
                                      self.cache.pages)
+            elif self.kind == "kivi2":
+                s4kv.s4kv_kivi2_quantize_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
+                                                wl.shared_prefix, bt, self.cache.pages,
+                                                scratch.tail_k, scratch.tail_v)
             else:
                 s4kv.s4kv_quantize_append(pshape, pk.contiguous(), pv.contiguous(), cu, sl,
                                           wl.shared_prefix, bt, self.cache.pages, scratch.tail_k,
@@ -113,7 +121,7 @@ class LayerCase:
     # ------------------------------------------------------------- oracle side
     def oracle_seq(self, b):
         k, v = self.seq_kv(b)
-        return oracle.sequence_cache(k.cpu().numpy(), v.cpu().numpy())
+        return oracle.sequence_cache(k.cpu().numpy(), v.cpu().numpy(), self.bits)
 
     def oracle_out(self, b, heads=None):
         c = self.oracle_seq(b)
@@ -130,7 +138,7 @@ class LayerCase:
         return oracle.decode_attention(q, kh, vh)
 
     def gpu_chunks(self, b):
-        """uint8 [full_b, Hkv, STRIDE] of sequence b's full pages."""
+        """uint8 [full_b, Hkv, stride] of sequence b's full pages (int4 or 2-bit pool)."""
         full = int(self.ctx[b]) // self.wl.page
         ids = self.plan.block_table[b, :full]
         return self.cache.chunk_view()[torch.from_numpy(ids.astype(np.int64)).cuda()].cpu().numpy()

@@ -132,3 +132,73 @@ def write_fp8_chunk(kc, vc):
     out[~is_v] = np.asarray(kc, dtype=np.uint8)[tok[~is_v], ch[~is_v]]
     out[is_v] = np.asarray(vc, dtype=np.uint8)[tok[is_v], ch[is_v]]
     return out
+
+
+# ---- 2-bit KIVI pool: 1600 data bytes + 64 padding per (page, KV head) ----
+K2_CHUNK_BYTES, K2_CHUNK_STRIDE = 1600, 1664
+K2_OFF_KC, K2_OFF_VC, K2_OFF_KS, K2_OFF_KZ, K2_OFF_VS, K2_OFF_VZ = 0, 512, 1024, 1280, 1536, 1568
+
+
+def _k2_maps():
+    """Code index n = 4 * byte + (bit offset within the byte) / 2 of a 2-bit
+    code block -> (token, channel), from the header's text: lane L = 16 g + c
+    owns bytes 8 L .. 8 L + 7 as words dd = 0, 1 (little endian); K word dd
+    holds channel 32 m + 8 g + i (m = 2 dd + mm) of token c at bit 8 mm +
+    2 (i >> 1) + 16 (i & 1); V word dd holds channel 16 (4 dd + s) + c of
+    token 4 g + k at bit 4 s + 2 (k >> 1) + 16 (k & 1)."""
+    ktok = np.empty(2048, dtype=np.int64)
+    kch = np.empty(2048, dtype=np.int64)
+    vtok = np.empty(2048, dtype=np.int64)
+    vch = np.empty(2048, dtype=np.int64)
+    for L in range(64):
+        g, c = L // 16, L % 16
+        for dd in range(2):
+            word0 = 16 * (2 * L + dd)            # first code index of this 32-bit word
+            for mm in range(2):
+                for i in range(8):
+                    n = word0 + (8 * mm + 2 * (i >> 1) + 16 * (i & 1)) // 2
+                    ktok[n], kch[n] = c, 32 * (2 * dd + mm) + 8 * g + i
+            for s in range(4):
+                for k in range(4):
+                    n = word0 + (4 * s + 2 * (k >> 1) + 16 * (k & 1)) // 2
+                    vtok[n], vch[n] = 4 * g + k, 16 * (4 * dd + s) + c
+    return ktok, kch, vtok, vch
+
+
+K2_KTOK, K2_KCH, K2_VTOK, K2_VCH = _k2_maps()
+
+
+def _codes2(block):
+    """uint8 [..., 512] -> uint8 [..., 2048], lowest bits first within each byte."""
+    return np.stack([(block >> (2 * j)) & 3 for j in range(4)], axis=-1).reshape(*block.shape[:-1], 2048)
+
+
+def read_chunks2(raw):
+    """raw: uint8 [..., 1664] (2-bit pool) -> the dict read_chunks returns."""
+    raw = np.asarray(raw, dtype=np.uint8)
+    lead = raw.shape[:-1]
+    ck = np.zeros(lead + (PAGE, D), dtype=np.uint8)
+    cv = np.zeros(lead + (PAGE, D), dtype=np.uint8)
+    ck[..., K2_KTOK, K2_KCH] = _codes2(raw[..., K2_OFF_KC:K2_OFF_KC + 512])
+    cv[..., K2_VTOK, K2_VCH] = _codes2(raw[..., K2_OFF_VC:K2_OFF_VC + 512])
+    u16 = lambda a, b: np.ascontiguousarray(raw[..., a:b]).view(np.uint16)
+    return {
+        "ck": ck, "cv": cv,
+        "sk": u16(K2_OFF_KS, K2_OFF_KS + 256), "zk": u16(K2_OFF_KZ, K2_OFF_KZ + 256),
+        "sv": u16(K2_OFF_VS, K2_OFF_VS + 32), "zv": u16(K2_OFF_VZ, K2_OFF_VZ + 32),
+        "pad": raw[..., K2_CHUNK_BYTES:K2_CHUNK_STRIDE],
+    }
+
+
+def write_chunk2(ck, sk, zk, cv, sv, zv):
+    """Logical 2-bit page (one KV head) -> uint8 [1664] (checker self-tests only)."""
+    raw = np.zeros(K2_CHUNK_STRIDE, dtype=np.uint8)
+    for off, codes in ((K2_OFF_KC, np.asarray(ck, np.uint8)[K2_KTOK, K2_KCH]),
+                       (K2_OFF_VC, np.asarray(cv, np.uint8)[K2_VTOK, K2_VCH])):
+        q = codes.reshape(512, 4)
+        raw[off:off + 512] = q[:, 0] | (q[:, 1] << 2) | (q[:, 2] << 4) | (q[:, 3] << 6)
+    raw[K2_OFF_KS:K2_OFF_KS + 256] = np.asarray(sk, dtype=np.float16).view(np.uint8)
+    raw[K2_OFF_KZ:K2_OFF_KZ + 256] = np.asarray(zk, dtype=np.float16).view(np.uint8)
+    raw[K2_OFF_VS:K2_OFF_VS + 32] = np.asarray(sv, dtype=np.float16).view(np.uint8)
+    raw[K2_OFF_VZ:K2_OFF_VZ + 32] = np.asarray(zv, dtype=np.float16).view(np.uint8)
+    return raw

@@ -15,11 +15,12 @@ TOL_MAX_ABS = 2e-3
 TOL_REL_L2 = 1e-3
 
 
-def page_mismatches(gpu_raw, oracle_pages):
+def page_mismatches(gpu_raw, oracle_pages, bits=4):
     """Compare GPU chunks (uint8 [n, Hkv, STRIDE]) with oracle pages
     (flush_pages output with leading dims [n, Hkv]). Returns a list of
-    (field, count) for fields that differ; empty when bit-exact."""
-    got = layout.read_chunks(gpu_raw)
+    (field, count) for fields that differ; empty when bit-exact. bits=2 reads
+    the 2-bit page format."""
+    got = layout.read_chunks(gpu_raw) if bits == 4 else layout.read_chunks2(gpu_raw)
     bad = []
     for key in ("ck", "cv"):
         n = int(np.count_nonzero(got[key] != oracle_pages[key]))

@@ -85,3 +85,13 @@ def test_mq_bytes():
     assert A.mq_bytes(ctx, [1, 1], 12, 3) == A.decode_bytes(ctx, 12, 3) + 4 * 3
     # each extra token adds its Q row and O row (fp16, Hq x 128)
     assert A.mq_bytes(ctx, [4, 2], 12, 3) - A.mq_bytes(ctx, [1, 1], 12, 3) == 4 * 4 * 12 * 128
+
+
+def test_kivi2_bytes():
+    # 2-bit pages: 32 + 32 B of codes per token, 4 B of V metadata per token,
+    # 512 B of K metadata per page = 100 B per token per KV head, 5.12x fp16
+    assert A.K2_CHUNK_BYTES == 1600 and A.K2_CHUNK_BYTES / 16 == 32 + 32 + 4 + 32
+    assert A.FP16_TOKEN_BYTES / (A.K2_CHUNK_BYTES / 16) == 5.12
+    assert A.cache_bytes([37], 3, A.K2_CHUNK_BYTES) == 3 * (2 * 1600 + 5 * 512)
+    b = A.decode_bytes(np.array([37]), 12, 3, A.K2_CHUNK_BYTES)
+    assert b == A.cache_bytes([37], 3, A.K2_CHUNK_BYTES) + 4 * 2 + 4 + 2 * (2 * 12 * 128)

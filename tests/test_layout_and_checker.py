@@ -99,3 +99,32 @@ def test_fp8_write_read_roundtrip():
     raw = layout.write_fp8_chunk(kc, vc)
     k2, v2 = layout.read_fp8_chunks(raw[None])
     assert np.array_equal(k2[0], kc) and np.array_equal(v2[0], vc)
+
+
+def test_k2_code_maps_are_bijections():
+    for tok, ch in ((layout.K2_KTOK, layout.K2_KCH), (layout.K2_VTOK, layout.K2_VCH)):
+        assert len(set(zip(tok.tolist(), ch.tolist()))) == 16 * 128
+    # lane 17 (g = 1, c = 1), word 0: K bits 0-1 are channel 8 of token 1, bits
+    # 16-17 channel 9, bits 8-9 channel 32 + 8
+    n0 = 16 * (2 * 17)
+    assert (layout.K2_KTOK[n0], layout.K2_KCH[n0]) == (1, 8)
+    assert (layout.K2_KTOK[n0 + 8], layout.K2_KCH[n0 + 8]) == (1, 9)
+    assert (layout.K2_KTOK[n0 + 4], layout.K2_KCH[n0 + 4]) == (1, 40)
+    # V word 1 of lane 33 (g = 2, c = 1): bits 4-5 are channel 16 * 5 + 1 of token 8
+    n1 = 16 * (2 * 33 + 1)
+    assert (layout.K2_VTOK[n1 + 2], layout.K2_VCH[n1 + 2]) == (8, 81)
+
+
+def test_k2_write_read_roundtrip_and_checker():
+    r = np.random.default_rng(4)
+    k = r.standard_normal((16, 128)).astype(np.float16)
+    v = r.standard_normal((16, 128)).astype(np.float16)
+    pg = oracle.flush_pages(k, v, bits=2)
+    raw = layout.write_chunk2(pg["ck"], pg["sk"], pg["zk"], pg["cv"], pg["sv"], pg["zv"])
+    got = layout.read_chunks2(raw[None])
+    assert np.array_equal(got["ck"][0], pg["ck"]) and np.array_equal(got["cv"][0], pg["cv"])
+    want = {kk: vv[None, None] for kk, vv in pg.items()}
+    assert parity.page_mismatches(raw[None, None], want, bits=2) == []
+    bad = raw.copy()
+    bad[700] ^= 0x04                                   # one V code changes
+    assert parity.page_mismatches(bad[None, None], want, bits=2)

@@ -18,6 +18,8 @@ import numpy as np
 PAGE = 16
 HEAD_DIM = 128
 CHUNK_BYTES = 2 * (PAGE * HEAD_DIM // 2) + 2 * 2 * HEAD_DIM + 2 * 2 * PAGE   # 2624
+# 2-bit KIVI pages: codes 16 x 128 x 2 bits for K and V, same metadata
+K2_CHUNK_BYTES = 2 * (PAGE * HEAD_DIM // 4) + 2 * 2 * HEAD_DIM + 2 * 2 * PAGE  # 1600
 FP16_TOKEN_BYTES = 2 * HEAD_DIM * 2                                           # K + V, 512
 
 
@@ -34,23 +36,24 @@ def density_vs_fp16():
     return FP16_TOKEN_BYTES / int4_bytes_per_token_per_head()
 
 
-def cache_bytes(ctx_lens, kv_heads):
+def cache_bytes(ctx_lens, kv_heads, chunk_bytes=CHUNK_BYTES):
     """Bytes of the int4 cache (full pages) plus the fp16 tail, one layer,
-    counting every sequence's pages (shared pages counted once per reader)."""
+    counting every sequence's pages (shared pages counted once per reader).
+    chunk_bytes=K2_CHUNK_BYTES counts 2-bit pages."""
     ctx = np.asarray(ctx_lens, dtype=np.int64)
     full = ctx // PAGE
     tail = ctx % PAGE
-    return int(kv_heads * (full.sum() * CHUNK_BYTES + tail.sum() * FP16_TOKEN_BYTES))
+    return int(kv_heads * (full.sum() * chunk_bytes + tail.sum() * FP16_TOKEN_BYTES))
 
 
-def decode_bytes(ctx_lens, num_q_heads, kv_heads):
+def decode_bytes(ctx_lens, num_q_heads, kv_heads, chunk_bytes=CHUNK_BYTES):
     """Algorithmic HBM bytes of one decode launch (one layer): the cache read
     (pages and tails), the block-table entries of the full pages, the context
     lengths, Q read and O written (fp16)."""
     ctx = np.asarray(ctx_lens, dtype=np.int64)
     b = len(ctx)
     full = ctx // PAGE
-    return int(cache_bytes(ctx, kv_heads) + 4 * full.sum() + 4 * b
+    return int(cache_bytes(ctx, kv_heads, chunk_bytes) + 4 * full.sum() + 4 * b
                + 2 * (2 * b * num_q_heads * HEAD_DIM))
 
 
