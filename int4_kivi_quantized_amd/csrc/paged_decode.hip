@@ -513,21 +513,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // wave-uniform, so the range and cursor arithmetic stays scalar
     U = (int64_t)hkv * __builtin_amdgcn_readfirstlane(local);
   }
-  // the 64-bit divisions run on the vector unit; bring the results back to
-  // scalar registers so every per-pair range check stays scalar
-  auto uniform64 = [](int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
-    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-  };
-  const int64_t u0 = uniform64((int64_t)w * U / W);
-  const int64_t u1 = uniform64((int64_t)(w + 1) * U / W);
+  // Unit indices fit in int32 (the host checks B * Hkv * (max_pages + 1)), so
+  // the cursors count in 32 bits and every per-pair range check is one scalar
+  // compare. The 64-bit divisions run on the vector unit; readfirstlane brings
+  // the results back to scalar registers.
+  const int32_t u0 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((int64_t)w * U / W));
+  const int32_t u1 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((int64_t)(w + 1) * U / W));
   const bool has_range = u0 < u1;
   if (w == 0 && lane == 0) total_units[0] = static_cast<int32_t>(U);
   if (!has_range) return;
   const int nchunks = (B + 63) / 64;
   int b0 = -1;
-  int64_t s0 = 0;  // first unit of sequence b0
+  int32_t s0 = 0;  // first unit of sequence b0
   {
     int64_t carry = 0;
     for (int k = 0; k < nchunks && b0 < 0; ++k) {
@@ -544,7 +541,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       if (past) {
         const int lf = __builtin_ctzll(past);
         b0 = 64 * k + lf;
-        s0 = (int64_t)hkv * (carry + __builtin_amdgcn_readfirstlane(__shfl(incl - n, lf)));
+        s0 = static_cast<int32_t>((int64_t)hkv * (carry + __builtin_amdgcn_readfirstlane(__shfl(incl - n, lf))));
       }
       carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
     }
@@ -568,7 +565,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // ---- cursors over the wave's units (all fields wave-uniform) ----
   struct Cursor {
-    int64_t u;   // flat index of the next unit
+    int32_t u;   // flat index of the next unit
     int b, h;    // sequence, KV head
     int unit;    // unit inside (b, h)
     int full;    // full pages of b
@@ -586,9 +583,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     start.u = u0;
     start.b = b0;
     seq_info(b0, start);
-    const int64_t local = u0 - s0;
-    start.h = static_cast<int>(local / start.nunits);
-    start.unit = static_cast<int>(local % start.nunits);
+    const int32_t local = u0 - s0;
+    start.h = local / start.nunits;
+    start.unit = local % start.nunits;
   }
   // Entry at a cursor: a pair (or single) of pages, or the tail.
   // Returns the number of units it covers (0 = tail).
@@ -641,15 +638,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   auto prefetch_ids = [&]() {
     if (!next_pair(prod)) return;
     // B * max_pages fits in int32 (the host checks B * Hkv * (max_pages + 1))
-    const int32_t* bt = block_table + (prod.b * max_pages + prod.unit);
-    nid_a = bt[0];
-    nid_b = (entry_pages(prod) == 2) ? bt[1] : nid_a;
+    // Both ids load unconditionally (the second index clamped to the row) and
+    // the pair / single choice is made where they are used, one pair later,
+    // so nothing waits for these scalar loads here.
+    const int32_t* row = block_table + prod.b * max_pages;
+    nid_a = row[prod.unit];
+    nid_b = row[min(prod.unit + 1, max_pages - 1)];
   };
   // Issue the pair at the producer cursor (tails need no DMA).
   auto produce = [&]() {
     if (prod.u >= u1) return;
     const int np = entry_pages(prod);
-    const int idA = nid_a, idB = nid_b;
+    const int idA = nid_a, idB = (np == 2) ? nid_b : nid_a;
     // chunk index id * Hkv + h < num_pages * Hkv fits in 32 bits
     const uint8_t* chA = pages + static_cast<uint64_t>(static_cast<uint32_t>(idA * hkv + prod.h)) * PF::kStride;
     const uint8_t* chB = pages + static_cast<uint64_t>(static_cast<uint32_t>(idB * hkv + prod.h)) * PF::kStride;
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     cur_b = b;
     cur_h = h;
     // the owner of the segment's first unit records the waves sharing it
-    const int64_t first = cu.u - cu.unit;
+    const int32_t first = cu.u - cu.unit;
     if (first >= u0 && lane == 0)
       seg_waves[(int64_t)b * hkv + h] = make_int2(owner_wave(first, U, W), owner_wave(first + cu.nunits - 1, U, W));
     // the query of the new (b, h); loading it waits for the ring's DMAs,
