@@ -279,12 +279,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Fmt::kWavesP
     for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
     U = (int64_t)hkv * __builtin_amdgcn_readfirstlane(local);
   }
-  const int64_t u0 = (int64_t)w * U / W;
-  const int64_t u1 = (int64_t)(w + 1) * U / W;
+  // Unit indices fit in int32 (the host checks B * Hkv * (max_pages + 1)): the
+  // cursors count in 32 bits, so every range check is one scalar compare.
+  const int32_t u0 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((int64_t)w * U / W));
+  const int32_t u1 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((int64_t)(w + 1) * U / W));
   if (w == 0 && lane == 0) total_units[0] = static_cast<int32_t>(U);
   if (u0 >= u1) return;
   int b0 = -1;
-  int64_t s0 = 0;  // first unit of sequence b0
+  int32_t s0 = 0;  // first unit of sequence b0
   {
     int64_t carry = 0;
     for (int k = 0; k < (B + 63) / 64 && b0 < 0; ++k) {
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Fmt::kWavesP
       if (past) {
         const int lf = __builtin_ctzll(past);
         b0 = 64 * k + lf;
-        s0 = (int64_t)hkv * (carry + __builtin_amdgcn_readfirstlane(__shfl(incl - n, lf)));
+        s0 = static_cast<int32_t>((int64_t)hkv * (carry + __builtin_amdgcn_readfirstlane(__shfl(incl - n, lf))));
       }
       carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
     }
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Fmt::kWavesP
   const int64_t page_stride = (int64_t)hkv * kChunk;
 
   struct Cursor {
-    int64_t u;   // flat index of the next unit
+    int32_t u;   // flat index of the next unit
     int b, h;    // sequence, KV head
     int unit;    // page inside (b, h)
     int npages;  // pages of b
@@ -334,8 +336,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Fmt::kWavesP
   start.u = u0;
   start.b = b0;
   seq_info(b0, start);
-  start.h = static_cast<int>((u0 - s0) / start.npages);
-  start.unit = static_cast<int>((u0 - s0) % start.npages);
+  start.h = (u0 - s0) / start.npages;
+  start.unit = (u0 - s0) % start.npages;
   auto advance = [&](Cursor& cu) {
     ++cu.u;
     if (++cu.unit >= cu.npages && cu.u < u1) {
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Fmt::kWavesP
   auto begin_segment = [&](const Cursor& cu) {
     cur_b = cu.b;
     cur_h = cu.h;
-    const int64_t first = cu.u - cu.unit;
+    const int32_t first = cu.u - cu.unit;
     if (first >= u0 && lane == 0)
       seg_waves[(int64_t)cu.b * hkv + cu.h] =
           make_int2(owner_wave(first, U, W), owner_wave(first + cu.npages - 1, U, W));
