@@ -221,3 +221,71 @@ def test_probe_refuses_before_launch():
     assert lib.s4kv_probe_read(fake, 4095, fake, 1, 1, 1, None) == s4kv.S4KV_ERR_INVALID_ARG
     assert lib.s4kv_probe_read(fake, 1 << 20, fake, 0, 1, 1, None) == s4kv.S4KV_ERR_INVALID_ARG
     assert lib.s4kv_probe_read(fake, 1 << 20, fake, 1, 0, 1, None) == s4kv.S4KV_ERR_INVALID_ARG
+
+
+def test_kivi2_sizes_and_refusals():
+    sh = Shape(**GOOD)
+    assert s4kv.s4kv_kivi2_pool_bytes(sh) == 100 * 8 * 1664
+    assert s4kv.s4kv_kivi2_pool_bytes(Shape(**{**GOOD, "head_dim": 64})) == 0
+    lib, P, fake = _raw_calls()
+    good = Shape(**GOOD).c()
+    bad = Shape(**{**GOOD, "num_q_heads": 12}).c()
+    args = [fake, fake, fake, fake, 1, fake, fake, fake, fake, None]
+    assert lib.s4kv_kivi2_quantize_append(ctypes.byref(bad), *args) == s4kv.S4KV_ERR_UNSUPPORTED
+    for i in (0, 1, 2, 3, 5, 6, 7, 8):
+        a = list(args)
+        a[i] = None
+        assert lib.s4kv_kivi2_quantize_append(ctypes.byref(good), *a) == s4kv.S4KV_ERR_INVALID_ARG
+    a = list(args)
+    a[4] = 64 * 16 + 1
+    assert lib.s4kv_kivi2_quantize_append(ctypes.byref(good), *a) == s4kv.S4KV_ERR_INVALID_ARG
+    a[4] = 0
+    assert lib.s4kv_kivi2_quantize_append(ctypes.byref(good), *a) == s4kv.S4KV_OK
+    ws = s4kv.s4kv_decode_workspace_bytes(Shape(**GOOD), 1000)
+
+    def call(shape=good, max_ctx=1000, ws_bytes=ws, null_at=None):
+        ptrs = [fake] * 6
+        if null_at is not None:
+            ptrs[null_at] = None
+        q, pages, tk, tv, bt, cl = ptrs
+        return lib.s4kv_kivi2_paged_decode(ctypes.byref(shape), q, pages, tk, tv, bt, cl, max_ctx,
+                                           ctypes.c_float(0.088), fake, fake, ws_bytes, None)
+
+    assert call(shape=bad) == s4kv.S4KV_ERR_UNSUPPORTED
+    assert call(max_ctx=0) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(max_ctx=64 * 16 + 1) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 1) == s4kv.S4KV_ERR_WORKSPACE
+    for i in range(6):
+        assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG
+
+
+def test_mq_workspace_and_refusals():
+    sh = Shape(**GOOD)                                   # G = 32 / 8 = 4
+    w1 = s4kv.s4kv_mq_workspace_bytes(sh, 1000, 1)
+    assert w1 == s4kv.s4kv_decode_workspace_bytes(sh, 1000)   # one token: the decode workspace
+    assert s4kv.s4kv_mq_workspace_bytes(sh, 1000, 4) > w1
+    assert s4kv.s4kv_mq_workspace_bytes(sh, 1000, 5) == 0     # 5 x 4 columns > 16
+    assert s4kv.s4kv_mq_workspace_bytes(sh, 1000, 0) == 0
+    assert s4kv.s4kv_mq_workspace_bytes(sh, 0, 1) == 0
+    lib, P, fake = _raw_calls()
+    good = Shape(**GOOD).c()
+    ws = s4kv.s4kv_mq_workspace_bytes(sh, 1000, 4)
+
+    def call(max_q=4, total_q=16, max_ctx=1000, ws_bytes=ws, null_at=None, shape=good):
+        ptrs = [fake] * 9
+        if null_at is not None:
+            ptrs[null_at] = None
+        q, cu, pages, tk, tv, bt, cl, out, wsp = ptrs
+        return lib.s4kv_paged_attention_mq(ctypes.byref(shape), q, cu, max_q, total_q, pages, tk, tv,
+                                           bt, cl, max_ctx, ctypes.c_float(0.088), out, wsp, ws_bytes,
+                                           None)
+
+    assert call(max_q=5) == s4kv.S4KV_ERR_UNSUPPORTED
+    assert call(max_q=0) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(total_q=0) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(total_q=4 * 4 + 1) == s4kv.S4KV_ERR_INVALID_ARG     # more rows than B * max_q
+    assert call(max_ctx=0) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 1) == s4kv.S4KV_ERR_WORKSPACE
+    assert call(shape=Shape(**{**GOOD, "page_size": 8}).c()) == s4kv.S4KV_ERR_UNSUPPORTED
+    for i in range(9):
+        assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG
