@@ -1,0 +1,75 @@
+"""The append and decode calls under HIP graph capture (torch.cuda.graph).
+
+The C ABI allocates nothing and never synchronizes, so one decode step (append
+one token per sequence, then decode) can be captured once and replayed: each
+replay appends the next token (slot, context and token values are updated in
+place between replays, with eager work and synchronizations in between) and
+must give exactly what the same calls give eagerly, step after step.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workload as W
+from tests.gpu_harness import LayerCase
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("kind", ["int4", "kivi2", "fp8"])
+def test_captured_step_replays_match_eager(kind):
+    print(f"[case] captured_step kind={kind}", flush=True)
+    base = W.WORKLOADS["llama3.2-3b-layer"]
+    wl = W.Workload("graph-3b", 1, 16, base.hq, base.hkv, base.ctx, base.k_outliers, seed=base.seed)
+    ctx0 = W.context_lengths(wl)
+    steps = 6
+    eager = LayerCase(wl, ctx_lens=ctx0, extra_tokens=steps, kind=kind)
+    graph = LayerCase(wl, ctx_lens=ctx0, extra_tokens=steps, kind=kind)
+    if kind == "fp8":
+        graph.cache.k_scale.copy_(eager.cache.k_scale)
+        graph.cache.v_scale.copy_(eager.cache.v_scale)
+    eager.prefill()
+    graph.prefill()
+    max_ctx = int(ctx0.max()) + steps
+    cu = torch.arange(wl.batch + 1, dtype=torch.int32, device="cuda")
+    # inputs the graph reads, updated in place between replays
+    slot = torch.tensor(ctx0.astype(np.int32), device="cuda")
+    ctx = slot + 1
+    k_in = torch.empty((wl.batch, wl.hkv, wl.head_dim), dtype=torch.float16, device="cuda")
+    v_in = torch.empty_like(k_in)
+    out = torch.empty_like(graph.q)
+    graph.cache.workspace(max_ctx)
+    # warm the library (device attributes are read once, outside any capture)
+    eager.cache.decode(eager.q, eager.block_table, eager.ctx_gpu, max_ctx)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    k0, v0 = W.new_tokens(wl, 0, 100, "cuda", graph.mult)
+    k_in.copy_(k0)
+    v_in.copy_(v0)
+    with torch.cuda.graph(g):
+        graph.cache.append(k_in, v_in, cu, slot, 1, graph.block_table)
+        graph.cache.decode(graph.q, graph.block_table, ctx, max_ctx, out=out)
+    torch.cuda.synchronize()
+    # capturing records the kernels without running them: replay s is step s
+
+    for s in range(steps):
+        k, v = W.new_tokens(wl, 0, s, "cuda", graph.mult)
+        k_in.copy_(k)
+        v_in.copy_(v)
+        slot.copy_(torch.tensor((ctx0 + s).astype(np.int32), device="cuda"))
+        ctx.copy_(slot + 1)
+        g.replay()
+        # eager twin of the same step, with its own buffers
+        sl_e = torch.tensor((ctx0 + s).astype(np.int32), device="cuda")
+        eager.cache.append(k.contiguous(), v.contiguous(), cu, sl_e, 1, eager.block_table)
+        ref = eager.cache.decode(eager.q, eager.block_table, sl_e + 1, max_ctx)
+        junk = torch.randn(1 << 16, device="cuda").sum()          # unrelated eager work
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(out, ref), f"replay {s}: output differs from the eager step"
+        assert torch.equal(graph.cache.pages, eager.cache.pages), f"replay {s}: pages differ"
+        if kind != "fp8":
+            assert torch.equal(graph.cache.tail_k, eager.cache.tail_k), f"replay {s}: tail K differs"
+            assert torch.equal(graph.cache.tail_v, eager.cache.tail_v), f"replay {s}: tail V differs"
