@@ -12,8 +12,9 @@
 // int4 page or the fp16 tail of (b, h). A fixed grid of W one-wave
 // work-groups (as many as the GPU keeps resident) splits the list into W equal
 // contiguous ranges; every wave derives the per-sequence unit counts and its
-// own range from the context lengths. Each wave streams its range through a 3-stage HBM -> LDS DMA ring,
-// pairing consecutive pages of the same (b, h), and keeps an online softmax
+// own range from the context lengths. Each wave streams its range through an HBM -> LDS DMA ring
+// (one stage in flight while one is computed), pairing consecutive pages of
+// the same (b, h), and keeps an online softmax
 // (running max in log2 units, running sum, unnormalized output) for the G
 // query heads of the current (b, h); each (b, h) its range touches yields a
 // partial result in workspace slot (b*Hkv + h) + wave.
@@ -208,17 +209,19 @@ __device__ inline void zero_terms(const h8 (&qh)[4], const u4 (&z)[4], float& ta
 }
 
 // A stage holds one pair of pages, copied HBM -> LDS by the DMA path
-// (global_load_lds_dwordx4: lane l writes 16 bytes at stage base + 16 l):
+// (global_load_lds_dwordx4: lane l writes 16 bytes at stage base + 16 l).
+// Every DMA copies from one chunk, so its source is a wave-uniform base plus
+// the lane's offset; the chunks' metadata (576 bytes) takes 36 lanes:
 //   [   0,1024) K codes page A     [1024,2048) K codes page B
 //   [2048,3072) V codes page A     [3072,4096) V codes page B
-//   [4096,4608) K scale+zero A     [4608,5120) K scale+zero B
-//   [5120,5184) V scale+zero A     [5184,5248) V scale+zero B
+//   [4096,4608) K scale+zero A     [4608,4672) V scale+zero A
+//   [4672,5184) K scale+zero B     [5184,5248) V scale+zero B
 //
 // With 2-bit pages a stage is:
-//   [   0, 512) K codes page A     [ 512,1024) K codes page B
-//   [1024,1536) V codes page A     [1536,2048) V codes page B
-//   [2048,2560) K scale+zero A     [2560,3072) K scale+zero B
-//   [3072,3136) V scale+zero A     [3136,3200) V scale+zero B
+//   [   0, 512) K codes page A     [ 512,1024) V codes page A
+//   [1024,1536) K codes page B     [1536,2048) V codes page B
+//   [2048,2560) K scale+zero A     [2560,2624) V scale+zero A
+//   [2624,3136) K scale+zero B     [3136,3200) V scale+zero B
 // kStages (per code width): the wave reads a stage into registers and
 // refills it at once, so the next pairs load while this one is computed.
 
@@ -231,7 +234,7 @@ template <int kBits>
 struct PairFmt;
 template <>
 struct PairFmt<4> {
-  static constexpr int kStageBytes = 5248, kDmaPerStage = 6, kKMeta = 4096, kVMeta = 5120;
+  static constexpr int kStageBytes = 5248, kDmaPerStage = 6;
   static constexpr int kStride = kChunkStride;
   // one stage: deeper rings measured slower (more bytes in flight per wave
   // only queue longer at this rate)
@@ -241,7 +244,7 @@ struct PairFmt<4> {
 };
 template <>
 struct PairFmt<2> {
-  static constexpr int kStageBytes = 3200, kDmaPerStage = 4, kKMeta = 2048, kVMeta = 3072;
+  static constexpr int kStageBytes = 3200, kDmaPerStage = 4;
   static constexpr int kStride = kK2ChunkStride;
   static constexpr int kStages = 1;
   static constexpr float kQSlot23 = 0.015625f, kPSlot23 = 0.25f;  // 2^-6, 1/4
@@ -251,11 +254,22 @@ struct PairFmt<2> {
 // Every cache byte is read once: the loads carry the non-temporal policy (nt),
 // which streams them past the caches; on MI355X a pure read of 4 KB chunks
 // runs at about 6.8-7.0 TB/s this way against about 6.0 TB/s without it.
-constexpr int kNonTemporal = 2;
-__device__ inline void dma16(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
-                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0,
-                                   kNonTemporal);
+// 16 bytes per lane from base + off (base wave-uniform, held in SGPRs; off the
+// lane's 32-bit offset) to LDS at lds_base + 16 * lane, non-temporal. The
+// SGPR-base address form costs no 64-bit vector address arithmetic per load
+// (the compiler's own lowering of the builtin adds the lane offset to a
+// 64-bit VGPR address for every load). The compiler sets M0 (the LDS base)
+// for the operand; the s_nop is the wait state between that write and the
+// load that reads it.
+__device__ inline void dma16_at(const uint8_t* base, uint32_t off, uint8_t* lds_base) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)(lds_base)));
+  __asm__ __volatile__(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 nt"
+      :
+      : "v"(off), "s"(base), "{m0}"(m0)
+      : "memory");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -303,16 +317,16 @@ struct PackedStage {
 __device__ inline void read_stage_packed(uint32_t base, int lane, int g, int page, int zrow,
                                          PackedStage& r) {
   const uint32_t a_lane = base + 16 * lane;
-  const uint32_t a_v = base + 64 * page + 8 * g;
-  const uint32_t a_k = base + 512 * page + 16 * g;
-  const uint32_t a_z = base + 512 * zrow + 16 * g;
+  const uint32_t a_v = base + 576 * page + 8 * g;
+  const uint32_t a_k = base + 576 * page + 16 * g;
+  const uint32_t a_z = base + 576 * zrow + 16 * g;
   __asm__ __volatile__(
       "ds_read_b128 %0, %14\n\t"
       "ds_read_b128 %1, %14 offset:1024\n\t"
       "ds_read_b128 %2, %14 offset:2048\n\t"
       "ds_read_b128 %3, %14 offset:3072\n\t"
-      "ds_read_b64 %4, %15 offset:5120\n\t"
-      "ds_read_b64 %5, %15 offset:5152\n\t"
+      "ds_read_b64 %4, %15 offset:4608\n\t"
+      "ds_read_b64 %5, %15 offset:4640\n\t"
       "ds_read_b128 %6, %16 offset:4096\n\t"
       "ds_read_b128 %7, %16 offset:4160\n\t"
       "ds_read_b128 %8, %16 offset:4224\n\t"
@@ -356,8 +370,8 @@ __device__ inline void read_stage_wide(uint32_t base, int lane, int g, int zrow,
       "ds_read_b128 %1, %8 offset:1024\n\t"
       "ds_read_b128 %2, %8 offset:2048\n\t"
       "ds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b64 %4, %9 offset:5120\n\t"
-      "ds_read_b64 %5, %9 offset:5152\n\t"
+      "ds_read_b64 %4, %9 offset:4608\n\t"
+      "ds_read_b64 %5, %9 offset:4640\n\t"
       "ds_read_b64 %6, %9 offset:5184\n\t"
       "ds_read_b64 %7, %9 offset:5216\n\t"
       "s_waitcnt lgkmcnt(0)"
@@ -366,8 +380,8 @@ __device__ inline void read_stage_wide(uint32_t base, int lane, int g, int zrow,
       : "v"(a_lane), "v"(a_v)
       : "memory");
   read_kvec(base + 16 * g, r.scA);
-  read_kvec(base + 512 + 16 * g, r.scB);
-  read_kvec(base + 512 * zrow + 256 + 16 * g, r.ze);
+  read_kvec(base + 576 + 16 * g, r.scB);
+  read_kvec(base + 576 * zrow + 256 + 16 * g, r.ze);
 }
 
 // The same stages for 2-bit pages: a lane's codes are 8 bytes per page.
@@ -380,16 +394,16 @@ struct PackedStage2 {
 __device__ inline void read_stage_packed2(uint32_t base, int lane, int g, int page, int zrow,
                                           PackedStage2& r) {
   const uint32_t a_lane = base + 8 * lane;
-  const uint32_t a_v = base + 64 * page + 8 * g;
-  const uint32_t a_k = base + 512 * page + 16 * g;
-  const uint32_t a_z = base + 512 * zrow + 16 * g;
+  const uint32_t a_v = base + 576 * page + 8 * g;
+  const uint32_t a_k = base + 576 * page + 16 * g;
+  const uint32_t a_z = base + 576 * zrow + 16 * g;
   __asm__ __volatile__(
       "ds_read_b64 %0, %14\n\t"
-      "ds_read_b64 %1, %14 offset:512\n\t"
-      "ds_read_b64 %2, %14 offset:1024\n\t"
+      "ds_read_b64 %1, %14 offset:1024\n\t"
+      "ds_read_b64 %2, %14 offset:512\n\t"
       "ds_read_b64 %3, %14 offset:1536\n\t"
-      "ds_read_b64 %4, %15 offset:3072\n\t"
-      "ds_read_b64 %5, %15 offset:3104\n\t"
+      "ds_read_b64 %4, %15 offset:2560\n\t"
+      "ds_read_b64 %5, %15 offset:2592\n\t"
       "ds_read_b128 %6, %16 offset:2048\n\t"
       "ds_read_b128 %7, %16 offset:2112\n\t"
       "ds_read_b128 %8, %16 offset:2176\n\t"
@@ -427,11 +441,11 @@ __device__ inline void read_stage_wide2(uint32_t base, int lane, int g, int zrow
   const uint32_t a_v = base + 8 * g;
   __asm__ __volatile__(
       "ds_read_b64 %0, %8\n\t"
-      "ds_read_b64 %1, %8 offset:512\n\t"
-      "ds_read_b64 %2, %8 offset:1024\n\t"
+      "ds_read_b64 %1, %8 offset:1024\n\t"
+      "ds_read_b64 %2, %8 offset:512\n\t"
       "ds_read_b64 %3, %8 offset:1536\n\t"
-      "ds_read_b64 %4, %9 offset:3072\n\t"
-      "ds_read_b64 %5, %9 offset:3104\n\t"
+      "ds_read_b64 %4, %9 offset:2560\n\t"
+      "ds_read_b64 %5, %9 offset:2592\n\t"
       "ds_read_b64 %6, %9 offset:3136\n\t"
       "ds_read_b64 %7, %9 offset:3168\n\t"
       "s_waitcnt lgkmcnt(0)"
@@ -440,8 +454,8 @@ __device__ inline void read_stage_wide2(uint32_t base, int lane, int g, int zrow
       : "v"(a_lane), "v"(a_v)
       : "memory");
   read_kvec2(base + 16 * g, r.scA);
-  read_kvec2(base + 512 + 16 * g, r.scB);
-  read_kvec2(base + 512 * zrow + 256 + 16 * g, r.ze);
+  read_kvec2(base + 576 + 16 * g, r.scB);
+  read_kvec2(base + 576 * zrow + 256 + 16 * g, r.ze);
 }
 __device__ inline void read_packed(uint32_t base, int lane, int g, int page, int zrow, PackedStage& r) {
   read_stage_packed(base, lane, g, page, zrow, r);
@@ -655,20 +669,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const uint8_t* chB = pages + static_cast<uint64_t>(static_cast<uint32_t>(idB * hkv + prod.h)) * PF::kStride;
     uint8_t* st = stage_s[pstage];
     if (++pstage == kStages) pstage = 0;
+    const uint32_t lo = 16u * static_cast<uint32_t>(lane);
     if constexpr (kBits == 4) {
-      dma16(chA + kOffKCodes + 16 * lane, st + 0);
-      dma16(chB + kOffKCodes + 16 * lane, st + 1024);
-      dma16(chA + kOffVCodes + 16 * lane, st + 2048);
-      dma16(chB + kOffVCodes + 16 * lane, st + 3072);
-      dma16((lane < 32 ? chA : chB) + kOffKScale + 16 * (lane & 31), st + 4096);
-      if (lane < 8) dma16((lane < 4 ? chA : chB) + kOffVScale + 16 * (lane & 3), st + 5120);
+      dma16_at(chA, lo + kOffKCodes, st + 0);
+      dma16_at(chB, lo + kOffKCodes, st + 1024);
+      dma16_at(chA, lo + kOffVCodes, st + 2048);
+      dma16_at(chB, lo + kOffVCodes, st + 3072);
+      if (lane < 36) {
+        dma16_at(chA, lo + kOffKScale, st + 4096);
+        dma16_at(chB, lo + kOffKScale, st + 4672);
+      }
     } else {
-      // each 512-byte block: lanes 0..31 from page A, 32..63 from page B
-      const uint8_t* half = (lane < 32 ? chA : chB) + 16 * (lane & 31);
-      dma16(half + kOff2KCodes, st + 0);
-      dma16(half + kOff2VCodes, st + 1024);
-      dma16(half + kOff2KScale, st + 2048);
-      if (lane < 8) dma16((lane < 4 ? chA : chB) + kOff2VScale + 16 * (lane & 3), st + 3072);
+      dma16_at(chA, lo, st + 0);
+      dma16_at(chB, lo, st + 1024);
+      if (lane < 36) {
+        dma16_at(chA, lo + kOff2KScale, st + 2048);
+        dma16_at(chB, lo + kOff2KScale, st + 2624);
+      }
     }
     ++issued;
     advance(prod, np);
