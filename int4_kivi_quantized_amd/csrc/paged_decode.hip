@@ -60,6 +60,11 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -INFINITY;
+// Running max of a column that has seen no token yet: finite, so exp2(x - m)
+// needs no special case (a -inf logit still gives 0, and the first finite
+// logit, at most ~2^40 in magnitude for fp16 operands, replaces it with a
+// rescale factor of exactly 0).
+constexpr float kMEmpty = -1.0e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 // Codes are fed as c * 2^-24 (slots 0,1,4,5) and c * 2^-20 (slots 2,3,6,7);
 // the query side carries 2^-4 and 2^-8 on those slots so every product is
@@ -154,11 +159,19 @@ __device__ inline float rows_sum(float v) {
   auto t = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
   return bitsf(t[0]) + bitsf(t[1]);
 }
+// max(a, b) in one instruction: fmaxf on values that come from a lane permute
+// first quiets each operand (two more instructions), and the compiler turns
+// med3(a, b, +inf) back into that. The operands are never NaN here.
+__device__ inline float max2(float a, float b) {
+  float r;
+  __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ inline float rows_max(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
-  v = fmaxf(bitsf(r[0]), bitsf(r[1]));
+  v = max2(bitsf(r[0]), bitsf(r[1]));
   auto t = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
-  return fmaxf(bitsf(t[0]), bitsf(t[1]));
+  return max2(bitsf(t[0]), bitsf(t[1]));
 }
 // DPP row rotations (within rows of 16 lanes); every lane reads a valid
 // source, so no "old" value is needed.
@@ -695,7 +708,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // ---- per-(b, h) state, per column ----
   h8 qc[4];  // query of the column's head, pre-scaled for the code operands
   h8 qh[4];  // the same query, plain (zero-point term)
-  float m_run = kNegInf, l_part = 0.f, lz_part = 0.f;
+  float m_run = kMEmpty, l_part = 0.f, lz_part = 0.f;
   f4 o[8];
   int cur_b = -1, cur_h = 0;
 
@@ -723,7 +736,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int i = 0; i < 8; ++i)
         qc[m][i] = static_cast<_Float16>(static_cast<float>(v[i]) * (((i & 2) == 0) ? 0.0625f : PF::kQSlot23));
     }
-    m_run = kNegInf;
+    m_run = kMEmpty;
     l_part = 0.f;
     lz_part = 0.f;
 #pragma unroll
@@ -774,7 +787,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       // pages A and B of the pairs kept their own maxima: merge the two columns
       auto partner = [&](float v) { return kHiLoCols ? xor4(v, c) : xor8(v); };
       const float M = fmaxf(m_run, partner(m_run));
-      const float a = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      const float a = __builtin_amdgcn_exp2f(m_run - M);
       l *= a;
       lz *= a;
       l += partner(l);
@@ -824,7 +837,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const bool up = mb > m_run + PF::kLazy;
     if (__any(up)) {
       const float mnew = up ? mb : m_run;
-      const float alpha = (mnew == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
       l_part *= alpha;
       lz_part *= alpha;
 #pragma unroll
@@ -832,8 +845,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       m_run = mnew;
     }
   };
-  // subtrahend for exp2: a column that has seen no token yet has only -inf logits
-  auto m_sub = [&]() { return (m_run == kNegInf) ? 0.f : m_run; };
 
   // ---- fp16 tail of (cur_b, cur_h): logits and output products on fp16 values;
   // in packed layouts only page-A columns take it
@@ -861,7 +872,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
     mb = rows_max(mb);
     rescale_to(mb);
-    const float ms = m_sub();
+    const float ms = m_run;
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -913,11 +924,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     produce();
     compiler_fence();
   };
-  // fp16 (hi, lo) parts of x = p * s for output slot k (slots 2,3,6,7 carry 1/16)
+  // fp16 (hi, lo) parts of x = p * s for output slot k (slots 2,3,6,7 carry
+  // 1/16, applied to p: an exact power-of-2 scaling, so the product is the
+  // same, and s enters the mixed-precision fma as fp16 unconverted)
   auto ps_split = [&](float pk, _Float16 s, int k, _Float16& hi, _Float16& lo) {
-    const float sv = static_cast<float>(s) * (((k & 2) == 0) ? 1.0f : PF::kPSlot23);
-    hi = static_cast<_Float16>(__builtin_fmaf(pk, sv, 0.0f));
-    lo = static_cast<_Float16>(__builtin_fmaf(pk, sv, -static_cast<float>(hi)));
+    const float pf = pk * (((k & 2) == 0) ? 1.0f : PF::kPSlot23);
+    const float sv = static_cast<float>(s);
+    hi = static_cast<_Float16>(__builtin_fmaf(pf, sv, 0.0f));
+    lo = static_cast<_Float16>(__builtin_fmaf(pf, sv, -static_cast<float>(hi)));
   };
   // pos0: cache position of page A's first token
   auto process_pair = [&](const uint8_t* st, bool has_b, int pos0) {
@@ -952,7 +966,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
       const float mb = rows_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
       rescale_to(mb);
-      const float ms = m_sub();
+      const float ms = m_run;
       _Float16 hv[4], lv[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -1029,8 +1043,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
       mb = rows_max(mb);
       rescale_to(mb);
-      // with causal masks a column can still have seen no token (m_run = -inf)
-      const float msw = kMQ ? m_sub() : m_run;
+      const float msw = m_run;
       h8 bhi, blo;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
