@@ -165,6 +165,35 @@ s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void
                               int32_t max_ctx, float sm_scale, void* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* One decode step with its append fused in: s4kv_quantize_append of one new
+ * token per sequence followed by s4kv_paged_decode, as one call (one launch
+ * of the decode stream, then the split merge). The pages' method is the same
+ * (S4 KV product page, "Funktionsweise" steps 1 and 2): the new token joins
+ * the fp16 tail, or completes its page, which is then quantized by the rule
+ * above; attention then covers every cached token including the new one.
+ * Pages, tails and outputs are bit-identical to the two separate calls.
+ *
+ * Args (device pointers unless noted):
+ *   q            fp16 [B][Hq][128].
+ *   k_new, v_new fp16 [B][Hkv][128]: the new token of every sequence.
+ *   pages, tail_k, tail_v  the layer's cache; updated in place.
+ *   block_table  int32 [B][max_pages_per_seq]; must map the page that the
+ *                new token lands in.
+ *   ctx_lens     int32 [B]: cached tokens per sequence AFTER the append, so
+ *                the new token sits at position ctx_lens[b] - 1 and the
+ *                cache held ctx_lens[b] - 1 tokens on entry.
+ *   max_ctx, sm_scale, out, workspace, workspace_bytes, stream: as for
+ *                s4kv_paged_decode (same workspace size).
+ * Device preconditions: those of s4kv_paged_decode. A sequence with
+ * ctx_lens[b] <= 0 takes no token and gets an all-zero output. Calls that
+ * share the cache buffers must not overlap.
+ * Returns as s4kv_paged_decode. */
+s4kv_status s4kv_paged_decode_append(const s4kv_shape* shape, const void* q, const void* k_new,
+                                     const void* v_new, void* pages, void* tail_k, void* tail_v,
+                                     const int32_t* block_table, const int32_t* ctx_lens,
+                                     int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ---- 2-bit KIVI pages ----
  *
  * The same cache with 2-bit codes: the KIVI paper the KV-cache explainer

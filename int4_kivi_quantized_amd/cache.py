@@ -45,6 +45,18 @@ class LayerCache:
                                ctx_lens, max_ctx, sm_scale, out, self.workspace(max_ctx), stream)
         return out
 
+    def decode_append(self, q, k_new, v_new, block_table, ctx_lens, max_ctx, sm_scale=None,
+                      out=None, stream=None):
+        """Append one token per sequence (ctx_lens already count it) and decode."""
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(self.shape.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        s4kv.s4kv_paged_decode_append(self.shape, q, k_new, v_new, self.pages, self.tail_k,
+                                      self.tail_v, block_table, ctx_lens, max_ctx, sm_scale, out,
+                                      self.workspace(max_ctx), stream)
+        return out
+
     def mq_workspace(self, max_ctx, max_q):
         need = s4kv.s4kv_mq_workspace_bytes(self.shape, max_ctx, max_q)
         if need == 0:

@@ -97,6 +97,26 @@ s4kv_status s4kv_paged_decode(const s4kv_shape* shape, const void* q, const void
   return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
 }
 
+s4kv_status s4kv_paged_decode_append(const s4kv_shape* shape, const void* q, const void* k_new,
+                                     const void* v_new, void* pages, void* tail_k, void* tail_v,
+                                     const int32_t* block_table, const int32_t* ctx_lens,
+                                     int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
+    return S4KV_ERR_INVALID_ARG;
+  if (!q || !k_new || !v_new || !pages || !tail_k || !tail_v || !block_table || !ctx_lens || !out ||
+      !workspace)
+    return S4KV_ERR_INVALID_ARG;
+  if (workspace_bytes < s4kv::workspace_bytes(*shape)) return S4KV_ERR_WORKSPACE;
+  const hipError_t e = s4kv::launch_paged_decode_append(*shape, q, k_new, v_new, pages, tail_k,
+                                                        tail_v, block_table, ctx_lens, max_ctx,
+                                                        sm_scale, out, workspace,
+                                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
 size_t s4kv_kivi2_pool_bytes(const s4kv_shape* shape) {
   if (check_shape(shape) != S4KV_OK) return 0;
   return (size_t)shape->num_pages * shape->num_kv_heads * S4KV_K2_CHUNK_STRIDE;

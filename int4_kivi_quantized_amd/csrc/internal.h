@@ -65,6 +65,13 @@ hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void
 // Multi-query attention over the int4 cache: up to max_q query tokens per
 // sequence (max_q * Hq / Hkv <= 16), causal within the sequence.
 size_t mq_workspace_bytes(const s4kv_shape& s, int32_t max_q);
+// Append one token per sequence (position ctx_lens[b] - 1, from k_new /
+// v_new [B][Hkv][128]) and decode, in one launch of the decode stream.
+hipError_t launch_paged_decode_append(const s4kv_shape& s, const void* q, const void* k_new,
+                                      const void* v_new, void* pages, void* tail_k, void* tail_v,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                                      hipStream_t stream);
 hipError_t launch_paged_mq(const s4kv_shape& s, const void* q, const int32_t* cu_q, int32_t max_q,
                            int32_t total_q, const void* pages, const void* tail_k, const void* tail_v,
                            const int32_t* block_table, const int32_t* ctx_lens, int32_t max_ctx,

@@ -49,6 +49,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "page_quant.h"
 
 namespace s4kv {
 namespace {
@@ -506,14 +507,22 @@ constexpr int kSlotStride = kHeadDim + 4;  // 128 outputs, m, l, 2 pad (16-byte 
 // holds token v / gq and head v % gq of the group, and attends causally: token
 // t of the T_b new tokens of sequence b sits at position ctx_b - T_b + t and
 // sees the cache positions up to it.
-template <int G, bool kMQ, int kBits>
+//
+// kAppend (int4 decode only): the call first appends one token per sequence,
+// the token at cache position ctx_b - 1, from k_new / v_new [B][Hkv][128]. The
+// wave that owns the last unit of a (b, h) does that append: it stores the
+// token in the fp16 tail, or, when the token completes a page, quantizes the
+// page (15 tail tokens and the new one) into the pool and into its ring stage.
+// Either way it attends over the new token straight from its inputs.
+template <int G, bool kMQ, int kBits, bool kAppend>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
-    const __half* __restrict__ q, const uint8_t* __restrict__ pages,
-    const __half* __restrict__ tail_k, const __half* __restrict__ tail_v,
+    const __half* __restrict__ q, uint8_t* __restrict__ pages,
+    __half* __restrict__ tail_k, __half* __restrict__ tail_v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
     int32_t* __restrict__ total_units, int2* __restrict__ seg_waves, int32_t B, int32_t max_pages,
     int32_t hkv, float sm_scale, float* __restrict__ slots, const int32_t* __restrict__ cu_q,
-    int32_t gq, int32_t total_q) {
+    int32_t gq, int32_t total_q, const __half* __restrict__ k_new, const __half* __restrict__ v_new) {
+  static_assert(!kAppend || (kBits == 4 && !kMQ), "the fused append serves the int4 decode");
   constexpr bool kPacked = (G <= 8);    // columns split between the two pages of a pair
   constexpr bool kHiLoCols = (G <= 4);  // and between the hi / lo parts of the output operand
   const int w = blockIdx.x, W = gridDim.x;
@@ -850,17 +859,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // in packed layouts only page-A columns take it
   // tail_pos0: cache position of the tail's first token
   auto process_tail = [&](int tail_n, int tail_pos0) {
-    const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
-    const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + ((int64_t)cur_b * hkv + cur_h) * kPage * kHeadDim);
+    const int64_t bh = (int64_t)cur_b * hkv + cur_h;
+    const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + bh * kPage * kHeadDim);
+    const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + bh * kPage * kHeadDim);
+    // kAppend: the new token is tail slot tail_n - 1; it is read from the
+    // inputs (its tail store below is not ordered before this wave's loads)
+    const int slot_new = kAppend ? tail_n - 1 : -1;
+    const uint8_t* kn = nullptr;
+    const uint8_t* vn = nullptr;
+    if constexpr (kAppend) {
+      kn = reinterpret_cast<const uint8_t*>(k_new + bh * kHeadDim);
+      vn = reinterpret_cast<const uint8_t*>(v_new + bh * kHeadDim);
+      // lanes 0..15 store its K row, lanes 16..31 its V row, 16 bytes each
+      if (lane < 32) {
+        __half* row = (lane < 16 ? tail_k : tail_v) + (bh * kPage + slot_new) * kHeadDim;
+        *reinterpret_cast<u4*>(reinterpret_cast<uint8_t*>(row) + 16 * (lane & 15)) =
+            ld16((lane < 16 ? kn : vn) + 16 * (lane & 15));
+      }
+    }
     _Float16 (*tv_s)[kHeadDim] = tail_s;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      reinterpret_cast<u4*>(&tv_s[0][0])[lane + 64 * i] = ld16(tv + 16 * (lane + 64 * i));
+    for (int i = 0; i < 4; ++i) {
+      const int piece = lane + 64 * i;  // 16-byte piece of the 16 x 256-byte rows
+      const uint8_t* src = (kAppend && (piece >> 4) == slot_new) ? vn + 16 * (piece & 15) : tv + 16 * piece;
+      reinterpret_cast<u4*>(&tv_s[0][0])[piece] = ld16(src);
+    }
     // logits: A = K tail values (token c, channels 32m+8g..+8), B = plain q
+    const uint8_t* krow = (kAppend && c == slot_new) ? kn : tk + 2 * c * kHeadDim;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc = mfma(as_h8(ld16(tk + 2 * (c * kHeadDim + 32 * m + 8 * g))), qh[m], acc);
+    for (int m = 0; m < 4; ++m) acc = mfma(as_h8(ld16(krow + 2 * (32 * m + 8 * g))), qh[m], acc);
     float lg[4];
     float mb = kNegInf;
 #pragma unroll
@@ -1077,8 +1106,45 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // 6 x (pairs issued after this one)" outstanding means this pair has landed
   // in LDS; other outstanding operations (query and tail loads,
   // partial-result stores) can only make the wait stricter.
-  auto consume_pair = [&](int np, int pos0) {
+  // kAppend, a (b, h) whose new token completes page P: quantize P from the 15
+  // tail tokens and the new one, store it in the pool, and put it into the
+  // stage in place of the copy the DMA brought from the pool (page B of a
+  // pair, or both copies of a single page). The tail's LDS area is the scratch.
+  auto fresh_page = [&](uint8_t* st, bool pair, int P) {
+    const int64_t bh = (int64_t)cur_b * hkv + cur_h;
+    const __half* tkb = tail_k + bh * kPage * kHeadDim;
+    const __half* tvb = tail_v + bh * kPage * kHeadDim;
+    const __half* kn = k_new + bh * kHeadDim;
+    const __half* vn = v_new + bh * kHeadDim;
+    auto krow = [&](int t) { return t < kPage - 1 ? tkb + t * kHeadDim : kn; };
+    auto vrow = [&](int t) { return t < kPage - 1 ? tvb + t * kHeadDim : vn; };
+    uint8_t (*scr)[kHeadDim] = reinterpret_cast<uint8_t (*)[kHeadDim]>(&tail_s[0][0]);
+    PageShare<4> sh;
+    quantize_page<4>(krow, vrow, lane, scr, scr + kPage, sh);
+    const int32_t id = block_table[cur_b * max_pages + P];
+    store_page<4>(pages + static_cast<uint64_t>(static_cast<uint32_t>(id * hkv + cur_h)) * PF::kStride,
+                  lane, sh, true);
+    auto to_stage = [&](int which) {
+      *reinterpret_cast<uint4*>(st + 1024 * which + 16 * lane) = sh.kcode;
+      *reinterpret_cast<uint4*>(st + 2048 + 1024 * which + 16 * lane) = sh.vcode;
+      uint8_t* meta = st + 4096 + 576 * which;
+      reinterpret_cast<__half2*>(meta)[lane] = sh.ks;
+      reinterpret_cast<__half2*>(meta + (kOffKZero - kOffKScale))[lane] = sh.kz;
+      if ((lane & 3) == 0) {
+        reinterpret_cast<__half*>(meta + (kOffVScale - kOffKScale))[lane >> 2] = sh.vs;
+        reinterpret_cast<__half*>(meta + (kOffVZero - kOffKScale))[lane >> 2] = sh.vz;
+      }
+    };
+    to_stage(1);
+    if (!pair) to_stage(0);
+    wait_lgkmcnt0();
+  };
+  auto consume_pair = [&](int np, int pos0, int fresh_p) {
     wait_pages_after<PF::kDmaPerStage, kStages - 1>(issued - consumed - 1);
+    compiler_fence();
+    if constexpr (kAppend) {
+      if (fresh_p >= 0) fresh_page(stage_s[cstage], np == 2, fresh_p);
+    }
     compiler_fence();
     process_pair(stage_s[cstage], np == 2, pos0);
     if (++cstage == kStages) cstage = 0;
@@ -1094,7 +1160,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // the segment's pages, then its tail if the range reaches it
     int np = entry_pages(cons);
     while (np > 0) {
-      consume_pair(np, cons.unit * kPage);
+      // kAppend: with no tail, the segment's last page holds the new token
+      const int fresh_p = (kAppend && cons.tail == 0 && cons.unit + np == cons.full) ? cons.full - 1 : -1;
+      consume_pair(np, cons.unit * kPage, fresh_p);
       advance(cons, np);
       np = (cons.u < u1 && cons.b == cur_b && cons.h == cur_h) ? entry_pages(cons) : -1;
     }
@@ -1193,33 +1261,38 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   *reinterpret_cast<uint2*>(o) = pk;
 }
 
-template <int G, bool kMQ, int kBits>
+// pages and tails are written only by the kAppend instantiations, whose
+// callers pass writable buffers
+template <int G, bool kMQ, int kBits, bool kAppend>
 hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages,
                     const void* tail_k, const void* tail_v, const int32_t* block_table,
                     const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves, float sm_scale,
                     float* slots, const int32_t* cu_q, int32_t gq, int32_t total_q,
-                    hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<G, kMQ, kBits>), dim3(W), dim3(64), 0, stream,
-                     static_cast<const __half*>(q), static_cast<const uint8_t*>(pages),
-                     static_cast<const __half*>(tail_k), static_cast<const __half*>(tail_v),
+                    const void* k_new, const void* v_new, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_stream_kernel<G, kMQ, kBits, kAppend>), dim3(W), dim3(64), 0, stream,
+                     static_cast<const __half*>(q), static_cast<uint8_t*>(const_cast<void*>(pages)),
+                     static_cast<__half*>(const_cast<void*>(tail_k)),
+                     static_cast<__half*>(const_cast<void*>(tail_v)),
                      block_table, ctx_lens, total_units, seg_waves, s.num_seqs, s.max_pages_per_seq,
-                     s.num_kv_heads, sm_scale, slots, cu_q, gq, total_q);
+                     s.num_kv_heads, sm_scale, slots, cu_q, gq, total_q,
+                     static_cast<const __half*>(k_new), static_cast<const __half*>(v_new));
   return hipGetLastError();
 }
 
 // one instantiation per column count 1..16
-template <bool kMQ, int kBits>
+template <bool kMQ, int kBits, bool kAppend = false>
 hipError_t launch_columns(int G, const s4kv_shape& s, int W, const void* q, const void* pages,
                           const void* tail_k, const void* tail_v, const int32_t* block_table,
                           const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves,
                           float sm_scale, float* slots, const int32_t* cu_q, int32_t gq,
-                          int32_t total_q, hipStream_t stream) {
+                          int32_t total_q, hipStream_t stream, const void* k_new = nullptr,
+                          const void* v_new = nullptr) {
   switch (G) {
 #define S4KV_CASE(g)                                                                             \
   case g:                                                                                        \
-    return launch_g<g, kMQ, kBits>(s, W, q, pages, tail_k, tail_v, block_table, ctx_lens,       \
-                                   total_units,                                                  \
-                                   seg_waves, sm_scale, slots, cu_q, gq, total_q, stream);
+    return launch_g<g, kMQ, kBits, kAppend>(s, W, q, pages, tail_k, tail_v, block_table,         \
+                                            ctx_lens, total_units, seg_waves, sm_scale, slots,  \
+                                            cu_q, gq, total_q, k_new, v_new, stream);
     S4KV_CASE(1) S4KV_CASE(2) S4KV_CASE(3) S4KV_CASE(4) S4KV_CASE(5) S4KV_CASE(6) S4KV_CASE(7)
     S4KV_CASE(8) S4KV_CASE(9) S4KV_CASE(10) S4KV_CASE(11) S4KV_CASE(12) S4KV_CASE(13)
     S4KV_CASE(14) S4KV_CASE(15) S4KV_CASE(16)
@@ -1317,6 +1390,22 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
           : launch_columns<false, 4>(G, s, W, q, pages, tail_k, tail_v, block_table, ctx_lens,
                                      ws.total_units, reinterpret_cast<int2*>(ws.seg_waves), sm_scale,
                                      ws.slots, nullptr, G, s.num_seqs, stream);
+  if (e != hipSuccess) return e;
+  return launch_split_merge(s, W, max_ctx, ws, ctx_lens, out, stream);
+}
+
+hipError_t launch_paged_decode_append(const s4kv_shape& s, const void* q, const void* k_new,
+                                      const void* v_new, void* pages, void* tail_k, void* tail_v,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                                      hipStream_t stream) {
+  const SplitWorkspace ws = split_workspace(s, workspace);
+  const int W = resident_waves();
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const hipError_t e = launch_columns<false, 4, true>(
+      G, s, W, q, pages, tail_k, tail_v, block_table, ctx_lens, ws.total_units,
+      reinterpret_cast<int2*>(ws.seg_waves), sm_scale, ws.slots, nullptr, G, s.num_seqs, stream,
+      k_new, v_new);
   if (e != hipSuccess) return e;
   return launch_split_merge(s, W, max_ctx, ws, ctx_lens, out, stream);
 }

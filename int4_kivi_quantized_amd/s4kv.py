@@ -99,6 +99,9 @@ def load():
     lib.s4kv_paged_decode.argtypes = [SP, P, P, P, P, P, P, I32, ctypes.c_float, P, P,
                                       ctypes.c_size_t, P]
     lib.s4kv_paged_decode.restype = ctypes.c_int
+    lib.s4kv_paged_decode_append.argtypes = [SP, P, P, P, P, P, P, P, P, I32, ctypes.c_float, P,
+                                             P, ctypes.c_size_t, P]
+    lib.s4kv_paged_decode_append.restype = ctypes.c_int
     lib.s4kv_fp16_pool_bytes.argtypes = [SP]
     lib.s4kv_fp16_pool_bytes.restype = ctypes.c_size_t
     lib.s4kv_fp16_append.argtypes = [SP, P, P, P, P, I32, P, P, P]
@@ -134,6 +137,7 @@ def load():
 EXPORTED = (
     "s4kv_validate", "s4kv_status_string", "s4kv_pool_bytes", "s4kv_tail_bytes",
     "s4kv_quantize_append", "s4kv_decode_workspace_bytes", "s4kv_paged_decode",
+    "s4kv_paged_decode_append",
     "s4kv_fp16_pool_bytes", "s4kv_fp16_append", "s4kv_fp16_paged_decode",
     "s4kv_fp8_pool_bytes", "s4kv_fp8_append", "s4kv_fp8_paged_decode",
     "s4kv_mq_workspace_bytes", "s4kv_paged_attention_mq",
@@ -213,6 +217,21 @@ def s4kv_paged_decode(shape, q, pages, tail_k, tail_v, block_table, ctx_lens, ma
         int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "s4kv_paged_decode")
+
+
+def s4kv_paged_decode_append(shape, q, k_new, v_new, pages, tail_k, tail_v, block_table, ctx_lens,
+                             max_ctx, sm_scale, out, workspace, stream=None):
+    """Append one token per sequence (k_new, v_new fp16 [B, Hkv, 128]; ctx_lens
+    count it) and decode, in one call; see s4kv.h."""
+    import torch
+    st = load().s4kv_paged_decode_append(
+        ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(k_new, torch.float16, "k_new"),
+        _ptr(v_new, torch.float16, "v_new"), _ptr(pages, torch.uint8, "pages"),
+        _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_lens, torch.int32, "ctx_lens"),
+        int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "s4kv_paged_decode_append")
 
 
 def s4kv_mq_workspace_bytes(shape, max_ctx, max_q):
