@@ -1,10 +1,13 @@
 """Benchmark of the int4 KIVI paged KV cache on one MI355X.
 
 A step is one decode step of the whole model-shaped stack: for every layer,
-s4kv_quantize_append of one new token per sequence (fp16 tail, page flush
-every 16th token) followed by s4kv_paged_decode over the int4 pages and the
-tail. Inputs (caches, queries, new tokens, context lengths) are resident in
-HBM before the timed region.
+one new token per sequence is appended (fp16 tail, page quantized when its
+16th token arrives) and attention runs over the int4 pages and the tail. By
+default each layer's step is one s4kv_paged_decode_append call (append and
+decode in one launch of the decode stream, then the split merge);
+--separate-append times s4kv_quantize_append followed by s4kv_paged_decode
+instead. Inputs (caches, queries, new tokens, context lengths) are resident
+in HBM before the timed region.
 
 Headline workload: Llama-3.1-8B-shaped decode, 32 layers, 32 query / 8 KV
 heads, head_dim 128, batch 128, contexts U[2048, 8192], page 16.
@@ -21,7 +24,8 @@ decode kernels' own load path, with and without the non-temporal policy).
 
 Prints one JSON line. `value` is KV GB/s: the algorithmic bytes of all decode
 launches of a step (pages, tails, block-table entries, Q, O) divided by the
-step time.
+step time. The appended tokens' own bytes (about 1 MB per 8B-shaped layer
+step) are not counted.
 """
 
 import argparse
@@ -104,7 +108,7 @@ class Model:
         torch.cuda.synchronize()
 
 
-def run_decode_bench(wl, steps, warmup, append):
+def run_decode_bench(wl, steps, warmup, append, fused=True):
     import torch
 
     total = steps + warmup
@@ -133,11 +137,15 @@ def run_decode_bench(wl, steps, warmup, append):
 
     def step(s, timed_idx=None):
         for layer, cache in enumerate(model.layers):
-            if append:
+            if append and not fused:
                 cache.append(new[layer][0], new[layer][1], cu1, slots[s], 1, model.bt)
             if timed_idx is not None:
                 ev_a[timed_idx * wl.layers + layer].record()
-            cache.decode(model.q[layer], model.bt, ctxs[s], max_ctx, out=outs[layer])
+            if append and fused:
+                cache.decode_append(model.q[layer], new[layer][0], new[layer][1], model.bt, ctxs[s],
+                                    max_ctx, out=outs[layer])
+            else:
+                cache.decode(model.q[layer], model.bt, ctxs[s], max_ctx, out=outs[layer])
             if timed_idx is not None:
                 ev_b[timed_idx * wl.layers + layer].record()
 
@@ -433,6 +441,9 @@ def main():
     ap.add_argument("--workload", default="llama3.1-8b-decode", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="time s4kv_quantize_append + s4kv_paged_decode per layer instead of the "
+                         "fused s4kv_paged_decode_append")
     ap.add_argument("--layers", type=int, default=None,
                     help="profiling only: override the workload's layer count (the JSON "
                          "line then does not describe the named workload)")
@@ -459,7 +470,8 @@ def main():
     rceil = read_ceiling()
     print(f"[bench] read ceiling {rceil['gbs']:.0f} GB/s (non-temporal), "
           f"{rceil['default_policy']['gbs']:.0f} GB/s (default policy)", file=sys.stderr, flush=True)
-    r = run_decode_bench(wl, args.steps, args.warmup, append=wl.append)
+    fused = wl.append and not args.separate_append
+    r = run_decode_bench(wl, args.steps, args.warmup, append=wl.append, fused=fused)
     del r["model"]
     torch.cuda.empty_cache()
     print(f"[bench] step {r['step_ms']:.3f} ms, {r['kv_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
@@ -483,14 +495,19 @@ def main():
             "workload": wl.name, "layers": wl.layers, "batch": wl.batch, "q_heads": wl.hq,
             "kv_heads": wl.hkv, "head_dim": wl.head_dim, "page": wl.page,
             "ctx": list(wl.ctx), "append_per_step": 1 if wl.append else 0,
+            "layer_step": ("s4kv_paged_decode_append" if fused else
+                           "s4kv_quantize_append + s4kv_paged_decode" if wl.append else
+                           "s4kv_paged_decode"),
             "profiling_layer_override": args.layers,
         },
         "hbm_peak_frac": round(r["kv_gbs"] / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(r["tokens_per_s"], 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "one s4kv_paged_decode call on one layer (its two launches: decode stream, "
-                      "split merge), timed with HIP events on the call's stream",
+            "kernel": ("one s4kv_paged_decode_append call on one layer (its two launches: decode "
+                       "stream with the one-token append, split merge)" if fused else
+                       "one s4kv_paged_decode call on one layer (its two launches: decode stream, "
+                       "split merge)") + ", timed with HIP events on the call's stream",
             "achieved": round(r["decode_launch_gbs"], 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -644,6 +644,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // ---- DMA ring ----
   __shared__ __align__(16) uint8_t stage_s[kStages][PF::kStageBytes];
   __shared__ __align__(16) _Float16 tail_s[kPage][kHeadDim];  // fp16 tail V, one (b, h) at a time
+  // kAppend: the raw K rows (bytes 0..4095) and V rows (4096..8191) of a page
+  // the new token completes: 15 tail rows and the new token as row 15
+  __shared__ __align__(16) uint8_t raw_s[kAppend ? 2 * kPage * 2 * kHeadDim : 16];
   Cursor prod = start;
   int issued = 0, consumed = 0;
   int pstage = 0, cstage = 0;  // ring slots of the next issue / the next consume
@@ -707,6 +710,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       if (lane < 36) {
         dma16_at(chA, lo + kOff2KScale, st + 2048);
         dma16_at(chB, lo + kOff2KScale, st + 2624);
+      }
+    }
+    if constexpr (kAppend) {
+      // the entry ends with the page the new token completes: bring its 15
+      // tail rows and the new token along with the stage, so the page is
+      // quantized from LDS when the entry is consumed (issued with the stage
+      // and before any later one, these loads are covered by its wait)
+      if (prod.tail == 0 && prod.unit + np == prod.full) {
+        const int64_t bh = (int64_t)prod.b * hkv + prod.h;
+        const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + bh * kPage * kHeadDim);
+        const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + bh * kPage * kHeadDim);
+        const uint8_t* kn = reinterpret_cast<const uint8_t*>(k_new + bh * kHeadDim);
+        const uint8_t* vn = reinterpret_cast<const uint8_t*>(v_new + bh * kHeadDim);
+        constexpr int kRow = 2 * kHeadDim;  // bytes per token row
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          dma16_at(tk, lo + 1024 * i, raw_s + 1024 * i);
+          dma16_at(tv, lo + 1024 * i, raw_s + kPage * kRow + 1024 * i);
+        }
+        if (lane < 48) {  // rows 12..14
+          dma16_at(tk, lo + 3072, raw_s + 3072);
+          dma16_at(tv, lo + 3072, raw_s + kPage * kRow + 3072);
+        }
+        if (lane < 16) {  // the new token, row 15
+          dma16_at(kn, lo, raw_s + (kPage - 1) * kRow);
+          dma16_at(vn, lo, raw_s + kPage * kRow + (kPage - 1) * kRow);
+        }
       }
     }
     ++issued;
@@ -1106,18 +1136,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // 6 x (pairs issued after this one)" outstanding means this pair has landed
   // in LDS; other outstanding operations (query and tail loads,
   // partial-result stores) can only make the wait stricter.
-  // kAppend, a (b, h) whose new token completes page P: quantize P from the 15
-  // tail tokens and the new one, store it in the pool, and put it into the
-  // stage in place of the copy the DMA brought from the pool (page B of a
-  // pair, or both copies of a single page). The tail's LDS area is the scratch.
+  // kAppend, a (b, h) whose new token completes page P: quantize P from its
+  // raw rows (in LDS with the stage), store it in the pool, and put it into
+  // the stage in place of the copy the DMA brought from the pool (page B of
+  // a pair, or both copies of a single page). The tail's LDS area is the
+  // scratch for the codes.
   auto fresh_page = [&](uint8_t* st, bool pair, int P) {
-    const int64_t bh = (int64_t)cur_b * hkv + cur_h;
-    const __half* tkb = tail_k + bh * kPage * kHeadDim;
-    const __half* tvb = tail_v + bh * kPage * kHeadDim;
-    const __half* kn = k_new + bh * kHeadDim;
-    const __half* vn = v_new + bh * kHeadDim;
-    auto krow = [&](int t) { return t < kPage - 1 ? tkb + t * kHeadDim : kn; };
-    auto vrow = [&](int t) { return t < kPage - 1 ? tvb + t * kHeadDim : vn; };
+    const __half* rk = reinterpret_cast<const __half*>(raw_s);
+    const __half* rv = reinterpret_cast<const __half*>(raw_s + kPage * 2 * kHeadDim);
+    auto krow = [&](int t) { return rk + t * kHeadDim; };
+    auto vrow = [&](int t) { return rv + t * kHeadDim; };
     uint8_t (*scr)[kHeadDim] = reinterpret_cast<uint8_t (*)[kHeadDim]>(&tail_s[0][0]);
     PageShare<4> sh;
     quantize_page<4>(krow, vrow, lane, scr, scr + kPage, sh);
