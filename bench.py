@@ -24,8 +24,10 @@ decode kernels' own load path, with and without the non-temporal policy).
 
 Prints one JSON line. `value` is KV GB/s: the algorithmic bytes of all decode
 launches of a step (pages, tails, block-table entries, Q, O) divided by the
-step time. The appended tokens' own bytes (about 1 MB per 8B-shaped layer
-step) are not counted.
+step time. With the fused call a launch's bytes include its one-token append
+(about 1.7 MB per 8B-shaped layer step: the new tokens, tail slots, and the
+pages they complete); with --separate-append the append kernel's bytes are
+not counted (its time is).
 """
 
 import argparse
@@ -165,8 +167,14 @@ def run_decode_bench(wl, steps, warmup, append, fused=True):
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
 
     # algorithmic bytes of the decode launches, per layer, averaged over timed steps
-    per_layer = [A.decode_bytes(model.ctx0 + (warmup + i + (1 if append else 0) if append else 0),
-                                wl.hq, wl.hkv) for i in range(steps)]
+    # (with the fused call, the launch's bytes also count its one-token append)
+    per_layer = []
+    for i in range(steps):
+        ctx_i = model.ctx0 + (warmup + i + 1 if append else 0)
+        nb = A.decode_bytes(ctx_i, wl.hq, wl.hkv)
+        if append and fused:
+            nb += A.append_step_bytes(ctx_i, wl.hkv)
+        per_layer.append(nb)
     dec_bytes = float(np.mean(per_layer))
     step_bytes = dec_bytes * wl.layers
     res = {

@@ -95,3 +95,12 @@ def test_kivi2_bytes():
     assert A.cache_bytes([37], 3, A.K2_CHUNK_BYTES) == 3 * (2 * 1600 + 5 * 512)
     b = A.decode_bytes(np.array([37]), 12, 3, A.K2_CHUNK_BYTES)
     assert b == A.cache_bytes([37], 3, A.K2_CHUNK_BYTES) + 4 * 2 + 4 + 2 * (2 * 12 * 128)
+
+
+def test_append_step_bytes():
+    """One token per sequence: read 512 B per KV head, then a 512-B tail write,
+    or for a completed page 15 tail tokens read and a 2624-B chunk written;
+    an empty sequence takes no token."""
+    ctx = [1, 16, 17, 0]
+    want = 2 * (3 * 512 + 2 * 512 + (15 * 512 + 2624))
+    assert A.append_step_bytes(ctx, 2) == want == 25728

@@ -57,6 +57,19 @@ def decode_bytes(ctx_lens, num_q_heads, kv_heads, chunk_bytes=CHUNK_BYTES):
                + 2 * (2 * b * num_q_heads * HEAD_DIM))
 
 
+def append_step_bytes(ctx_lens, kv_heads):
+    """Algorithmic bytes of appending one token to every sequence with
+    ctx_lens[b] >= 1 (ctx_lens count the new token): its fp16 K/V read, then
+    either its tail slot written or, when it completes a page, the page's 15
+    earlier tail tokens read and the page's int4 chunk written."""
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    live = ctx > 0
+    n = int(live.sum())
+    done = int((live & (ctx % PAGE == 0)).sum())
+    return int(kv_heads * (n * FP16_TOKEN_BYTES + (n - done) * FP16_TOKEN_BYTES
+                           + done * ((PAGE - 1) * FP16_TOKEN_BYTES + CHUNK_BYTES)))
+
+
 def fp16_decode_bytes(ctx_lens, num_q_heads, kv_heads):
     """Algorithmic HBM bytes of one fp16-cache decode launch (one layer): the
     fp16 K and V of every cached token, one block-table entry per page (full
