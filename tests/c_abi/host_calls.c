@@ -39,6 +39,8 @@ int main(void) {
         S4KV_ERR_INVALID_ARG);
   CHECK(s4kv_paged_decode(&bad, NULL, NULL, NULL, NULL, NULL, NULL, 16, 0.088f, NULL, NULL, 0,
                           NULL) == S4KV_ERR_UNSUPPORTED);
+  CHECK(s4kv_paged_decode_append(&s, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 16, 0.088f,
+                                 NULL, NULL, 0, NULL) == S4KV_ERR_INVALID_ARG);
   CHECK(s4kv_fp8_paged_decode(&s, NULL, NULL, NULL, NULL, 0, 0.088f, NULL, NULL, NULL, NULL, 0,
                               NULL) == S4KV_ERR_INVALID_ARG);
   CHECK(s4kv_probe_read(NULL, 4096, NULL, 1, 1, 1, NULL) == S4KV_ERR_INVALID_ARG);

@@ -133,6 +133,29 @@ def test_decode_refuses_before_launch():
         assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG
 
 
+def test_decode_append_refuses_before_launch():
+    lib, P, fake = _raw_calls()
+    good = Shape(**GOOD).c()
+    ws = s4kv.s4kv_decode_workspace_bytes(Shape(**GOOD), 1000)
+
+    def call(shape=good, max_ctx=1000, ws_bytes=ws, null_at=None):
+        ptrs = [fake] * 9
+        if null_at is not None:
+            ptrs[null_at] = None
+        q, kn, vn, pages, tk, tv, bt, cl, out = ptrs
+        return lib.s4kv_paged_decode_append(ctypes.byref(shape), q, kn, vn, pages, tk, tv, bt, cl,
+                                            max_ctx, ctypes.c_float(0.088), out, fake, ws_bytes,
+                                            None)
+
+    bad = Shape(**{**GOOD, "num_q_heads": 12}).c()
+    assert call(shape=bad) == s4kv.S4KV_ERR_UNSUPPORTED
+    assert call(max_ctx=0) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(max_ctx=64 * 16 + 1) == s4kv.S4KV_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 1) == s4kv.S4KV_ERR_WORKSPACE
+    for i in range(9):
+        assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG
+
+
 def test_fp16_append_refuses_before_launch():
     lib, P, fake = _raw_calls()
     bad = Shape(**{**GOOD, "num_kv_heads": 5}).c()

@@ -73,3 +73,48 @@ def test_captured_step_replays_match_eager(kind):
         if kind != "fp8":
             assert torch.equal(graph.cache.tail_k, eager.cache.tail_k), f"replay {s}: tail K differs"
             assert torch.equal(graph.cache.tail_v, eager.cache.tail_v), f"replay {s}: tail V differs"
+
+
+def test_captured_fused_step_replays_match_eager():
+    """The fused call (s4kv_paged_decode_append) captured once and replayed:
+    every replay appends the next token and attends, exactly as the same call
+    made eagerly on a twin cache."""
+    print("[case] captured_fused_step", flush=True)
+    base = W.WORKLOADS["llama3.2-3b-layer"]
+    wl = W.Workload("graph-fused-3b", 1, 16, base.hq, base.hkv, base.ctx, base.k_outliers, seed=base.seed)
+    ctx0 = W.context_lengths(wl)
+    steps = 18                                   # crosses a page completion for every sequence
+    eager = LayerCase(wl, ctx_lens=ctx0, extra_tokens=steps)
+    graph = LayerCase(wl, ctx_lens=ctx0, extra_tokens=steps)
+    eager.prefill()
+    graph.prefill()
+    max_ctx = int(ctx0.max()) + steps
+    ctx = torch.tensor((ctx0 + 1).astype(np.int32), device="cuda")
+    k_in = torch.empty((wl.batch, wl.hkv, wl.head_dim), dtype=torch.float16, device="cuda")
+    v_in = torch.empty_like(k_in)
+    out = torch.empty_like(graph.q)
+    graph.cache.workspace(max_ctx)
+    eager.cache.decode(eager.q, eager.block_table, eager.ctx_gpu, max_ctx)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graph.cache.decode_append(graph.q, k_in, v_in, graph.block_table, ctx, max_ctx, out=out)
+    torch.cuda.synchronize()
+
+    for s in range(steps):
+        k, v = W.new_tokens(wl, 0, s, "cuda", graph.mult)
+        k_in.copy_(k)
+        v_in.copy_(v)
+        ctx.copy_(torch.tensor((ctx0 + s + 1).astype(np.int32), device="cuda"))
+        g.replay()
+        ctx_e = torch.tensor((ctx0 + s + 1).astype(np.int32), device="cuda")
+        ref = eager.cache.decode_append(eager.q, k.contiguous(), v.contiguous(), eager.block_table,
+                                        ctx_e, max_ctx)
+        junk = torch.randn(1 << 16, device="cuda").sum()          # unrelated eager work
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(out, ref), f"replay {s}: output differs from the eager call"
+        assert torch.equal(graph.cache.pages, eager.cache.pages), f"replay {s}: pages differ"
+        assert torch.equal(graph.cache.tail_k, eager.cache.tail_k), f"replay {s}: tail K differs"
+        assert torch.equal(graph.cache.tail_v, eager.cache.tail_v), f"replay {s}: tail V differs"
