@@ -17,6 +17,8 @@
  *   - s4kv_paged_decode: one decode step of attention for every sequence over
  *     its int4 pages plus its fp16 tail (GQA, split over pages, cross-split
  *     softmax reduction);
+ *   - s4kv_paged_decode_append: the two above for one new token per
+ *     sequence, fused into the decode's launch (bit-identical results);
  *   - s4kv_fp16_append / s4kv_fp16_paged_decode: the same over an fp16 paged
  *     cache, the control path the int4 cache is measured against.
  *
