@@ -113,7 +113,9 @@ class Model:
 def run_decode_bench(wl, steps, warmup, append, fused=True):
     import torch
 
-    total = steps + warmup
+    # warm-up steps, the timed steps (no per-call events inside), then as many
+    # steps again with HIP events around every call for the per-call figures
+    total = warmup + 2 * steps
     model = Model(wl, total if append else 0, time_prefill=not append)
     B = wl.batch
     max_ctx = int(model.ctx0.max()) + (total if append else 0)
@@ -159,24 +161,29 @@ def run_decode_bench(wl, steps, warmup, append, fused=True):
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        step(warmup + i, i)
+        step(warmup + i)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = t0.elapsed_time(t1) / steps
+    # per-call durations: the next `steps` steps, each call between two events
+    for i in range(steps):
+        step(warmup + steps + i, i)
+    torch.cuda.synchronize()
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
 
     # algorithmic bytes of the decode launches, per layer, averaged over timed steps
     # (with the fused call, the launch's bytes also count its one-token append)
-    per_layer = []
-    for i in range(steps):
-        ctx_i = model.ctx0 + (warmup + i + 1 if append else 0)
-        nb = A.decode_bytes(ctx_i, wl.hq, wl.hkv)
+    def layer_bytes(s):
+        ctx_s = model.ctx0 + (s + 1 if append else 0)
+        nb = A.decode_bytes(ctx_s, wl.hq, wl.hkv)
         if append and fused:
-            nb += A.append_step_bytes(ctx_i, wl.hkv)
-        per_layer.append(nb)
-    dec_bytes = float(np.mean(per_layer))
-    step_bytes = dec_bytes * wl.layers
+            nb += A.append_step_bytes(ctx_s, wl.hkv)
+        return nb
+    per_layer = [layer_bytes(warmup + i) for i in range(steps)]            # timed steps
+    per_call = [layer_bytes(warmup + steps + i) for i in range(steps)]     # per-call steps
+    step_bytes = float(np.mean(per_layer)) * wl.layers
+    dec_bytes = float(np.mean(per_call))
     res = {
         "step_ms": step_ms,
         "wall_s": wall,
