@@ -21,6 +21,11 @@
 // splitk_reduce_kernel merges, for each (b, query head), the partials of the
 // consecutive waves whose ranges touched it.
 //
+// The same stream can first append one token per sequence (the decode step's
+// quantize-on-append, S4 KV product page, "Funktionsweise" step 1): the wave
+// owning the last unit of a (b, h) stores the token in the tail, or quantizes
+// the page it completes, and attends over it from its inputs (kAppend below).
+//
 // Dense contractions on v_mfma_f32_16x16x32_f16 (D = A x B, 16x32 by 32x16):
 //  * logits, transposed: S^T[token][col] = sum_d codeK[token][d] * qs[d][col]
 //    with qs = q * sK (the per-channel K scale folded into the query, per page)
