@@ -519,8 +519,10 @@ constexpr int kSlotStride = kHeadDim + 4;  // 128 outputs, m, l, 2 pad (16-byte 
 // token in the fp16 tail, or, when the token completes a page, quantizes the
 // page (15 tail tokens and the new one) into the pool and into its ring stage.
 // Either way it attends over the new token straight from its inputs.
+// Waves per SIMD: two, or three with 2-bit codes, whose pairs carry fewer
+// bytes for the same instruction count (the 2-bit kernel fits 168 VGPRs).
 template <int G, bool kMQ, int kBits, bool kAppend>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ? 3 : 2, kBits == 2 ? 3 : 2))) void decode_stream_kernel(
     const __half* __restrict__ q, uint8_t* __restrict__ pages,
     __half* __restrict__ tail_k, __half* __restrict__ tail_v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
@@ -1413,7 +1415,9 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
                                int32_t max_ctx, float sm_scale, void* out, void* workspace,
                                hipStream_t stream, int bits) {
   const SplitWorkspace ws = split_workspace(s, workspace);
-  const int W = resident_waves();
+  // 2-bit: three waves per SIMD (resident_waves() counts two); the workspace
+  // holds slots for kMaxWaves waves
+  const int W = (bits == 2) ? std::min(resident_waves() / 2 * 3, kMaxWaves) : resident_waves();
   const int G = s.num_q_heads / s.num_kv_heads;
   const hipError_t e =
       (bits == 2)
