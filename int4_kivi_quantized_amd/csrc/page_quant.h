@@ -84,11 +84,14 @@ struct PageShare {
 
 // Quantize the page whose token t has K row krow(t) and V row vrow(t)
 // (128 fp16 each). kc / vc: 16 x 128 bytes of LDS scratch for the codes.
-// Every lane of the wave must call it (it synchronizes the work-group, which
-// is this one wave).
-template <int kBits, class RowK, class RowV>
+// kmeta(out) / vmeta(out) are called as soon as the K / V scales and zeros
+// are known, so a caller can store them while the rest is computed. Every
+// lane of the wave must call it (it synchronizes the work-group, which is
+// this one wave).
+template <int kBits, class RowK, class RowV, class KMeta, class VMeta>
 __device__ inline void quantize_page(RowK krow, RowV vrow, int lane, uint8_t (*kc)[kHeadDim],
-                                     uint8_t (*vc)[kHeadDim], PageShare<kBits>& out) {
+                                     uint8_t (*vc)[kHeadDim], PageShare<kBits>& out, KMeta kmeta,
+                                     VMeta vmeta) {
   // K: lane owns channels 2*lane, 2*lane+1; groups run over the 16 tokens.
   float k0[kPage], k1[kPage];
 #pragma unroll
@@ -112,6 +115,7 @@ __device__ inline void quantize_page(RowK krow, RowV vrow, int lane, uint8_t (*k
   }
   out.ks = __halves2half2(g0.s, g1.s);
   out.kz = __halves2half2(g0.z, g1.z);
+  kmeta(out);
 
   // V: lane owns token t = lane/4, channels 32*(lane%4) .. +32; groups run
   // over the token's 128 channels (4 lanes per token).
@@ -139,6 +143,7 @@ __device__ inline void quantize_page(RowK krow, RowV vrow, int lane, uint8_t (*k
   for (int i = 0; i < 32; ++i) vc[vt][32 * vu + i] = static_cast<uint8_t>(code_of<kBits>(vx[i], gv));
   out.vs = gv.s;
   out.vz = gv.z;
+  vmeta(out);
   __syncthreads();
 
   if constexpr (kBits == 4) {
@@ -219,21 +224,35 @@ __device__ inline void quantize_page(RowK krow, RowV vrow, int lane, uint8_t (*k
 }
 
 // Store a lane's share of a page at chunk (the page's first byte; global or
-// LDS pointer); with zero_pad also the padding after the data.
+// LDS pointer): the K scales and zeros, the V scales and zeros (with
+// zero_pad also the padding after the data), the codes, or all of them.
 template <int kBits, class Ptr>
-__device__ inline void store_page(Ptr chunk, int lane, const PageShare<kBits>& in, bool zero_pad) {
+__device__ inline void store_page_kmeta(Ptr chunk, int lane, const PageShare<kBits>& in) {
   using C = Codes<kBits>;
-  using Block = typename C::Block;
-  reinterpret_cast<Block*>(chunk + C::kK)[lane] = in.kcode;
-  reinterpret_cast<Block*>(chunk + C::kV)[lane] = in.vcode;
   reinterpret_cast<__half2*>(chunk + C::kKs)[lane] = in.ks;
   reinterpret_cast<__half2*>(chunk + C::kKz)[lane] = in.kz;
+}
+template <int kBits, class Ptr>
+__device__ inline void store_page_vmeta(Ptr chunk, int lane, const PageShare<kBits>& in, bool zero_pad) {
+  using C = Codes<kBits>;
   if ((lane & 3) == 0) {
     reinterpret_cast<__half*>(chunk + C::kVs)[lane >> 2] = in.vs;
     reinterpret_cast<__half*>(chunk + C::kVz)[lane >> 2] = in.vz;
   }
   if (zero_pad && lane < (C::kStride - C::kData) / 4)
     reinterpret_cast<uint32_t*>(chunk + C::kData)[lane] = 0u;
+}
+template <int kBits, class Ptr>
+__device__ inline void store_page_codes(Ptr chunk, int lane, const PageShare<kBits>& in) {
+  using Block = typename Codes<kBits>::Block;
+  reinterpret_cast<Block*>(chunk + Codes<kBits>::kK)[lane] = in.kcode;
+  reinterpret_cast<Block*>(chunk + Codes<kBits>::kV)[lane] = in.vcode;
+}
+template <int kBits, class Ptr>
+__device__ inline void store_page(Ptr chunk, int lane, const PageShare<kBits>& in, bool zero_pad) {
+  store_page_codes<kBits>(chunk, lane, in);
+  store_page_kmeta<kBits>(chunk, lane, in);
+  store_page_vmeta<kBits>(chunk, lane, in, zero_pad);
 }
 
 }  // namespace s4kv

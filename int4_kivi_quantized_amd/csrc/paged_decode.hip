@@ -1155,7 +1155,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     auto vrow = [&](int t) { return rv + t * kHeadDim; };
     uint8_t (*scr)[kHeadDim] = reinterpret_cast<uint8_t (*)[kHeadDim]>(&tail_s[0][0]);
     PageShare<4> sh;
-    quantize_page<4>(krow, vrow, lane, scr, scr + kPage, sh);
+    auto none = [](const PageShare<4>&) {};
+    quantize_page<4>(krow, vrow, lane, scr, scr + kPage, sh, none, none);
     const int32_t id = block_table[cur_b * max_pages + P];
     store_page<4>(pages + static_cast<uint64_t>(static_cast<uint32_t>(id * hkv + cur_h)) * PF::kStride,
                   lane, sh, true);

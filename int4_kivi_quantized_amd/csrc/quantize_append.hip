@@ -72,8 +72,11 @@ __global__ __launch_bounds__(64) void quantize_append_kernel(
     auto krow = [&](int t) { return token_row(base + t, start, in_row0, h, hkv, k, tk); };
     auto vrow = [&](int t) { return token_row(base + t, start, in_row0, h, hkv, v, tv); };
     PageShare<kBits> share;
-    quantize_page<kBits>(krow, vrow, lane, kc, vc, share);
-    store_page<kBits>(chunk, lane, share, true);
+    // scales and zeros go out while the rest of the page is computed
+    quantize_page<kBits>(krow, vrow, lane, kc, vc, share,
+                         [&](const PageShare<kBits>& sh) { store_page_kmeta<kBits>(chunk, lane, sh); },
+                         [&](const PageShare<kBits>& sh) { store_page_vmeta<kBits>(chunk, lane, sh, true); });
+    store_page_codes<kBits>(chunk, lane, share);
   }
 
   if (x == 0 && (end % kPage) != 0) {
