@@ -251,9 +251,18 @@ __device__ inline void zero_terms(const h8 (&qh)[4], const u4 (&z)[4], float& ta
 // fp16 maximum 65504 (2^15.999).
 template <int kBits>
 struct PairFmt;
+//
+// kQExp: every column's query enters the code products pre-scaled by a power
+// of two 2^E with max_d |q_d| 2^E < 2^kQExp. With the 2^-4 slot factor, the
+// folded product q 2^E s then stays below 2^(kQExp - 4) times the largest
+// fp16 K scale, (65504 + 65504) / qmax rounded to fp16 (8736 for int4,
+// 43680 for 2 bits): 34944 and 43680, inside the fp16 range, so no fp16 query
+// and K page can overflow it. Small query components keep the resolution of
+// fp16's smallest subnormal relative to 2^E instead of to 1.
 template <>
 struct PairFmt<4> {
   static constexpr int kStageBytes = 5248, kDmaPerStage = 6;
+  static constexpr int kQExp = 6;
   static constexpr int kStride = kChunkStride;
   // one stage: deeper rings measured slower (more bytes in flight per wave
   // only queue longer at this rate)
@@ -264,6 +273,7 @@ struct PairFmt<4> {
 template <>
 struct PairFmt<2> {
   static constexpr int kStageBytes = 3200, kDmaPerStage = 4;
+  static constexpr int kQExp = 4;
   static constexpr int kStride = kK2ChunkStride;
   static constexpr int kStages = 1;
   static constexpr float kQSlot23 = 0.015625f, kPSlot23 = 0.25f;  // 2^-6, 1/4
@@ -605,6 +615,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   const int zrow = c >> 3;  // page of the K zeros this lane supplies (zero-term product)
   const float l2s = sm_scale * kLog2e;  // logits go to log2 units
   const float qk_scale = l2s * kQkUnscale;
+  float qk_col = qk_scale;  // qk_scale / 2^E for the column's query pre-scale 2^E
 
   // ---- cursors over the wave's units (all fields wave-uniform) ----
   struct Cursor {
@@ -772,15 +783,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     const uint8_t* qr = q_row(b, h, cu.full * kPage + cu.tail);
 #pragma unroll
     for (int m = 0; m < 4; ++m) raw[m] = ld16(qr + 2 * (32 * m + 8 * g));
+    // the column's pre-scale 2^E: E = kQExp - e with max_d |q_d| = f 2^e,
+    // f in [0.5, 1), so max |q| 2^E < 2^kQExp (E in [-10, 29] for fp16 q;
+    // a zero query gives E = kQExp)
+    float amax = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      // element i of product m is channel 32m+8g+i, pre-scaled by 2^-4
-      // (slots 0,1,4,5) or 2^-8 (slots 2,3,6,7)
       const h8 v = as_h8(raw[m]);
       qh[m] = v;
 #pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(static_cast<float>(v[i])));
+    }
+    const int E = PF::kQExp - __builtin_amdgcn_frexp_expf(rows_max(amax));
+    const float pre = __builtin_bit_cast(float, static_cast<uint32_t>(127 + E) << 23);
+    qk_col = qk_scale * __builtin_bit_cast(float, static_cast<uint32_t>(127 - E) << 23);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // element i of product m is channel 32m+8g+i, pre-scaled by 2^E times
+      // 2^-4 (slots 0,1,4,5) or the second slot group's factor (slots 2,3,6,7)
+#pragma unroll
       for (int i = 0; i < 8; ++i)
-        qc[m][i] = static_cast<_Float16>(static_cast<float>(v[i]) * (((i & 2) == 0) ? 0.0625f : PF::kQSlot23));
+        qc[m][i] = static_cast<_Float16>(static_cast<float>(qh[m][i]) * pre *
+                                         (((i & 2) == 0) ? 0.0625f : PF::kQSlot23));
     }
     m_run = kMEmpty;
     l_part = 0.f;
@@ -1024,7 +1048,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
       const f4 mine = pslot ? accB : accA;
       float lg[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) lg[k] = mine[k] * qk_scale + zl;
+      for (int k = 0; k < 4; ++k) lg[k] = mine[k] * qk_col + zl;
       if constexpr (kMQ) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
@@ -1099,8 +1123,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
       float mb = kNegInf;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        lgA[k] = accA[k] * qk_scale + zA * l2s;
-        lgB[k] = accB[k] * qk_scale + zlB;
+        lgA[k] = accA[k] * qk_col + zA * l2s;
+        lgB[k] = accB[k] * qk_col + zlB;
         if constexpr (kMQ) {
           if (pos0 + 4 * g + k > col_lim) lgA[k] = kNegInf;
           if (pos0 + kPage + 4 * g + k > col_lim) lgB[k] = kNegInf;
@@ -1340,16 +1364,15 @@ hipError_t launch_columns(int G, const s4kv_shape& s, int W, const void* q, cons
 }  // namespace
 
 int resident_waves() {
-  // one wave per work-group, two per SIMD, four SIMDs per CU
-  static int cached = 0;
-  if (cached == 0) {
+  // one wave per work-group, two per SIMD, four SIMDs per CU; the first call
+  // sizes it (a function-local static: its initialization is thread-safe)
+  static const int cached = [] {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    cached = cus * 8;
-    if (cached > kMaxWaves) cached = kMaxWaves;
-  }
+    return cus * 8 > kMaxWaves ? kMaxWaves : cus * 8;
+  }();
   return cached;
 }
 

@@ -181,6 +181,47 @@ def _ptr(t, dtype, name, device=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _numel(t, want, name, at_least=False):
+    """The C ABI sees only pointers: a tensor of the wrong size would make the
+    kernels read or write out of bounds, so sizes are checked here."""
+    n = t.numel()
+    if (n < want) if at_least else (n != want):
+        rel = "at least " if at_least else ""
+        raise ValueError(f"{name} has {n} elements, needs {rel}{want}")
+
+
+def _rows(t, row, name):
+    """Tensor holding whole rows of ``row`` elements; returns the row count."""
+    if t.numel() % row:
+        raise ValueError(f"{name} has {t.numel()} elements, not a multiple of {row}")
+    return t.numel() // row
+
+
+def _check_tables(shape, block_table, ctx_lens=None):
+    _numel(block_table, shape.num_seqs * shape.max_pages_per_seq, "block_table")
+    if ctx_lens is not None:
+        _numel(ctx_lens, shape.num_seqs, "ctx_lens")
+
+
+def _check_tails(shape, tail_k, tail_v):
+    n = shape.num_seqs * shape.num_kv_heads * PAGE_SIZE * HEAD_DIM
+    _numel(tail_k, n, "tail_k", at_least=True)
+    _numel(tail_v, n, "tail_v", at_least=True)
+
+
+def _check_new_tokens(shape, k, v, cu_new, slot):
+    row = shape.num_kv_heads * HEAD_DIM
+    if _rows(k, row, "k") != _rows(v, row, "v"):
+        raise ValueError("k and v must hold the same number of tokens")
+    _numel(cu_new, shape.num_seqs + 1, "cu_new")
+    _numel(slot, shape.num_seqs, "slot")
+
+
+def _check_q_out(shape, q, out):
+    _numel(q, shape.num_seqs * shape.num_q_heads * HEAD_DIM, "q")
+    _numel(out, shape.num_seqs * shape.num_q_heads * HEAD_DIM, "out")
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -197,6 +238,10 @@ def s4kv_quantize_append(shape, k, v, cu_new, slot, max_new, block_table, pages,
                          stream=None):
     """Append new K/V tokens (fp16 [total_new, Hkv, 128]) to every sequence; see s4kv.h."""
     import torch
+    _check_new_tokens(shape, k, v, cu_new, slot)
+    _check_tables(shape, block_table)
+    _numel(pages, s4kv_pool_bytes(shape), "pages", at_least=True)
+    _check_tails(shape, tail_k, tail_v)
     st = load().s4kv_quantize_append(
         ctypes.byref(shape.c()), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
         _ptr(cu_new, torch.int32, "cu_new"), _ptr(slot, torch.int32, "slot"), int(max_new),
@@ -210,6 +255,10 @@ def s4kv_paged_decode(shape, q, pages, tail_k, tail_v, block_table, ctx_lens, ma
                       out, workspace, stream=None):
     """One decode step: out fp16 [B, Hq, 128] from q fp16 [B, Hq, 128]; see s4kv.h."""
     import torch
+    _check_q_out(shape, q, out)
+    _check_tables(shape, block_table, ctx_lens)
+    _numel(pages, s4kv_pool_bytes(shape), "pages", at_least=True)
+    _check_tails(shape, tail_k, tail_v)
     st = load().s4kv_paged_decode(
         ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(pages, torch.uint8, "pages"),
         _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),
@@ -224,6 +273,12 @@ def s4kv_paged_decode_append(shape, q, k_new, v_new, pages, tail_k, tail_v, bloc
     """Append one token per sequence (k_new, v_new fp16 [B, Hkv, 128]; ctx_lens
     count it) and decode, in one call; see s4kv.h."""
     import torch
+    _check_q_out(shape, q, out)
+    _numel(k_new, shape.num_seqs * shape.num_kv_heads * HEAD_DIM, "k_new")
+    _numel(v_new, shape.num_seqs * shape.num_kv_heads * HEAD_DIM, "v_new")
+    _check_tables(shape, block_table, ctx_lens)
+    _numel(pages, s4kv_pool_bytes(shape), "pages", at_least=True)
+    _check_tails(shape, tail_k, tail_v)
     st = load().s4kv_paged_decode_append(
         ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(k_new, torch.float16, "k_new"),
         _ptr(v_new, torch.float16, "v_new"), _ptr(pages, torch.uint8, "pages"),
@@ -243,6 +298,12 @@ def s4kv_paged_attention_mq(shape, q, cu_q, max_q, pages, tail_k, tail_v, block_
     """Multi-query attention: out fp16 [total_q, Hq, 128] from q fp16 [total_q, Hq, 128], the
     rows of sequence b being cu_q[b] .. cu_q[b+1]-1 (int32 [B+1]); see s4kv.h."""
     import torch
+    _rows(q, shape.num_q_heads * HEAD_DIM, "q")
+    _numel(out, q.numel(), "out")
+    _numel(cu_q, shape.num_seqs + 1, "cu_q")
+    _check_tables(shape, block_table, ctx_lens)
+    _numel(pages, s4kv_pool_bytes(shape), "pages", at_least=True)
+    _check_tails(shape, tail_k, tail_v)
     st = load().s4kv_paged_attention_mq(
         ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(cu_q, torch.int32, "cu_q"),
         int(max_q), int(q.shape[0]), _ptr(pages, torch.uint8, "pages"),
@@ -260,6 +321,9 @@ def s4kv_fp16_pool_bytes(shape):
 def s4kv_fp16_append(shape, k, v, cu_new, slot, max_new, block_table, pages, stream=None):
     """Append new K/V tokens (fp16 [total_new, Hkv, 128]) to the fp16 pool; see s4kv.h."""
     import torch
+    _check_new_tokens(shape, k, v, cu_new, slot)
+    _check_tables(shape, block_table)
+    _numel(pages, s4kv_fp16_pool_bytes(shape) // 2, "pages", at_least=True)
     st = load().s4kv_fp16_append(
         ctypes.byref(shape.c()), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
         _ptr(cu_new, torch.int32, "cu_new"), _ptr(slot, torch.int32, "slot"), int(max_new),
@@ -272,6 +336,9 @@ def s4kv_fp16_paged_decode(shape, q, pages, block_table, ctx_lens, max_ctx, sm_s
                            workspace, stream=None):
     """One decode step over the fp16 pool: out fp16 [B, Hq, 128]; see s4kv.h."""
     import torch
+    _check_q_out(shape, q, out)
+    _check_tables(shape, block_table, ctx_lens)
+    _numel(pages, s4kv_fp16_pool_bytes(shape) // 2, "pages", at_least=True)
     st = load().s4kv_fp16_paged_decode(
         ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(pages, torch.float16, "pages"),
         _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_lens, torch.int32, "ctx_lens"),
@@ -289,6 +356,11 @@ def s4kv_fp8_append(shape, k, v, cu_new, slot, max_new, block_table, k_scale, v_
     """Quantize new K/V tokens (fp16 [total_new, Hkv, 128]) to E4M3 with the per-KV-head
     scales (fp32 [Hkv]) and append them to the FP8 pool; see s4kv.h."""
     import torch
+    _check_new_tokens(shape, k, v, cu_new, slot)
+    _check_tables(shape, block_table)
+    _numel(k_scale, shape.num_kv_heads, "k_scale")
+    _numel(v_scale, shape.num_kv_heads, "v_scale")
+    _numel(pages, s4kv_fp8_pool_bytes(shape), "pages", at_least=True)
     st = load().s4kv_fp8_append(
         ctypes.byref(shape.c()), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
         _ptr(cu_new, torch.int32, "cu_new"), _ptr(slot, torch.int32, "slot"), int(max_new),
@@ -302,6 +374,11 @@ def s4kv_fp8_paged_decode(shape, q, pages, block_table, ctx_lens, max_ctx, sm_sc
                           v_scale, out, workspace, stream=None):
     """One decode step over the FP8 pool: out fp16 [B, Hq, 128]; see s4kv.h."""
     import torch
+    _check_q_out(shape, q, out)
+    _check_tables(shape, block_table, ctx_lens)
+    _numel(k_scale, shape.num_kv_heads, "k_scale")
+    _numel(v_scale, shape.num_kv_heads, "v_scale")
+    _numel(pages, s4kv_fp8_pool_bytes(shape), "pages", at_least=True)
     st = load().s4kv_fp8_paged_decode(
         ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(pages, torch.uint8, "pages"),
         _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_lens, torch.int32, "ctx_lens"),
@@ -329,6 +406,10 @@ def s4kv_kivi2_quantize_append(shape, k, v, cu_new, slot, max_new, block_table, 
                                tail_v, stream=None):
     """s4kv_quantize_append with 2-bit codes into the 2-bit pool; see s4kv.h."""
     import torch
+    _check_new_tokens(shape, k, v, cu_new, slot)
+    _check_tables(shape, block_table)
+    _numel(pages, s4kv_kivi2_pool_bytes(shape), "pages", at_least=True)
+    _check_tails(shape, tail_k, tail_v)
     st = load().s4kv_kivi2_quantize_append(
         ctypes.byref(shape.c()), _ptr(k, torch.float16, "k"), _ptr(v, torch.float16, "v"),
         _ptr(cu_new, torch.int32, "cu_new"), _ptr(slot, torch.int32, "slot"), int(max_new),
@@ -342,6 +423,10 @@ def s4kv_kivi2_paged_decode(shape, q, pages, tail_k, tail_v, block_table, ctx_le
                             sm_scale, out, workspace, stream=None):
     """s4kv_paged_decode over the 2-bit pool; see s4kv.h."""
     import torch
+    _check_q_out(shape, q, out)
+    _check_tables(shape, block_table, ctx_lens)
+    _numel(pages, s4kv_kivi2_pool_bytes(shape), "pages", at_least=True)
+    _check_tails(shape, tail_k, tail_v)
     st = load().s4kv_kivi2_paged_decode(
         ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(pages, torch.uint8, "pages"),
         _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),

@@ -74,10 +74,55 @@ def test_decode_parity(name):
 
 # --------------------------------------------------------------- full size, sampled
 
-FULL = ["llama3.1-8b-decode", "qwen2.5-7b-shared-prefix", "llama3-70b"]
+def _check_layer_full(case):
+    """Every page and tail of every sequence bit-exact, and the output of every
+    sequence and query head within the attention bar; the oracle runs per
+    sequence on a thread pool (numpy releases the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    wl = case.wl
+    out = case.decode().float().cpu().numpy()
+    kvs = [tuple(x.cpu().numpy() for x in case.seq_kv(b)) for b in range(wl.batch)]
+    chunks = [case.gpu_chunks(b) for b in range(wl.batch)]
+    tails = [case.gpu_tail(b) for b in range(wl.batch)]
+    q = case.q.cpu().numpy()
+
+    def one(b):
+        c = oracle.sequence_cache(*kvs[b])
+        bad = parity.page_mismatches(chunks[b], c["pages"])
+        tk, tv = tails[b]
+        tail_ok = (np.array_equal(tk.view(np.uint16), c["tail_k"].view(np.uint16))
+                   and np.array_equal(tv.view(np.uint16), c["tail_v"].view(np.uint16)))
+        kh, vh = oracle.dequantized_sequence(c)
+        return bad, tail_ok, oracle.decode_attention(q[b], kh, vh)
+
+    with ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(one, range(wl.batch)))
+    for b, (bad, tail_ok, _) in enumerate(res):
+        assert not bad, f"seq {b}: page fields differ: {bad}"
+        assert tail_ok, f"seq {b}: tail differs"
+    ok, max_abs, rel = parity.attention_ok(out, np.stack([r[2] for r in res]))
+    print(f"  {wl.batch} sequences x {wl.hq} heads: pages and tails bit-exact, "
+          f"decode max_abs={max_abs:.2e} rel_l2={rel:.2e}", flush=True)
+    assert ok, f"attention out of tolerance: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,layer", [("llama3-70b", 0), ("llama3-70b", 79),
+                                        ("qwen2.5-7b-shared-prefix", 0)])
+def test_full_layer(name, layer):
+    """Whole layers: the first and last layer of the 70B-shaped workload (B16,
+    32K contexts, G = 8) and the shared-prefix layer (G = 7; aliased prefix
+    pages are read by every sharing sequence)."""
+    _print_case("full_layer", workload=name, layer=layer)
+    case = LayerCase(W.WORKLOADS[name], layer=layer)
+    case.prefill()
+    if len(case.plan.sharing):
+        b = int(case.plan.sharing[0])
+        assert set(case.plan.block_table[b, :4]) <= set(case.plan.prefix_pages.tolist())
+    _check_layer_full(case)
+
+
+@pytest.mark.parametrize("name", ["llama3.1-8b-decode"])
 def test_full_size_sampled(name):
     _print_case("full_size_sampled", workload=name)
     case = LayerCase(W.WORKLOADS[name])
