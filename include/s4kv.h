@@ -75,7 +75,9 @@ typedef enum s4kv_status {
   S4KV_ERR_UNSUPPORTED = 2, /* head_dim != 128, page_size != 16, Hq % Hkv != 0,
                                Hq / Hkv > 16: the model is refused */
   S4KV_ERR_WORKSPACE = 3,   /* decode workspace smaller than required */
-  S4KV_ERR_HIP = 4          /* a HIP launch failed (hipGetLastError) */
+  S4KV_ERR_HIP = 4,         /* a HIP launch failed (hipGetLastError) */
+  S4KV_ERR_SCRATCH_LIMIT = 5 /* s4kv_paged_decode_append_noalloc: the shape needs more
+                               decode workspace than S4KV_NOALLOC_SCRATCH_BYTES */
 } s4kv_status;
 
 typedef struct s4kv_shape {
@@ -195,6 +197,35 @@ s4kv_status s4kv_paged_decode_append(const s4kv_shape* shape, const void* q, con
                                      const int32_t* block_table, const int32_t* ctx_lens,
                                      int32_t max_ctx, float sm_scale, void* out, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/* ---- allocation-free decode step ----
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same call as s4kv_paged_decode_append (same arguments, same
+ * kernels, bit-identical results) with the decode workspace taken from a
+ * static array inside the library instead of an argument:
+ *   - one array of S4KV_NOALLOC_SCRATCH_BYTES per device, created when the
+ *     library's code is loaded on that device and held until the process
+ *     ends; its address is looked up on the first call on a device;
+ *   - a shape whose workspace (s4kv_decode_workspace_bytes) exceeds it is
+ *     refused with S4KV_ERR_SCRATCH_LIMIT before anything is enqueued (the
+ *     Llama-3.1-8B- and 70B-shaped decode steps need about 11 MB and 18 MB);
+ *   - the call allocates nothing and frees nothing; every call on one device
+ *     shares that device's array, and nothing in it needs to be cleared
+ *     between calls (the call writes every workspace word it later reads),
+ *     but calls that overlap on one device (different streams, or different
+ *     host threads, without ordering between them) race on it and give
+ *     undefined results;
+ *   - the stream must belong to the current device.
+ * Returns as s4kv_paged_decode_append, or S4KV_ERR_SCRATCH_LIMIT. */
+#define S4KV_NOALLOC_SCRATCH_BYTES (32u << 20)
+s4kv_status s4kv_paged_decode_append_noalloc(const s4kv_shape* shape, const void* q,
+                                             const void* k_new, const void* v_new, void* pages,
+                                             void* tail_k, void* tail_v,
+                                             const int32_t* block_table, const int32_t* ctx_lens,
+                                             int32_t max_ctx, float sm_scale, void* out,
+                                             void* stream);
 
 /* ---- 2-bit KIVI pages ----
  *

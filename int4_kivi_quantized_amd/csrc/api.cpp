@@ -42,6 +42,8 @@ const char* s4kv_status_string(s4kv_status status) {
     case S4KV_ERR_UNSUPPORTED: return "unsupported shape (needs head_dim 128, page 16, Hq % Hkv == 0, Hq/Hkv <= 16)";
     case S4KV_ERR_WORKSPACE: return "workspace too small";
     case S4KV_ERR_HIP: return "HIP launch failed";
+    case S4KV_ERR_SCRATCH_LIMIT:
+      return "shape needs more decode workspace than the static scratch (S4KV_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -114,6 +116,26 @@ s4kv_status s4kv_paged_decode_append(const s4kv_shape* shape, const void* q, con
                                                         tail_v, block_table, ctx_lens, max_ctx,
                                                         sm_scale, out, workspace,
                                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
+s4kv_status s4kv_paged_decode_append_noalloc(const s4kv_shape* shape, const void* q,
+                                             const void* k_new, const void* v_new, void* pages,
+                                             void* tail_k, void* tail_v,
+                                             const int32_t* block_table, const int32_t* ctx_lens,
+                                             int32_t max_ctx, float sm_scale, void* out,
+                                             void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
+    return S4KV_ERR_INVALID_ARG;
+  if (!q || !k_new || !v_new || !pages || !tail_k || !tail_v || !block_table || !ctx_lens || !out)
+    return S4KV_ERR_INVALID_ARG;
+  if (s4kv::workspace_bytes(*shape) > (size_t)S4KV_NOALLOC_SCRATCH_BYTES)
+    return S4KV_ERR_SCRATCH_LIMIT;
+  const hipError_t e = s4kv::launch_paged_decode_append_noalloc(
+      *shape, q, k_new, v_new, pages, tail_k, tail_v, block_table, ctx_lens, max_ctx, sm_scale,
+      out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
 }
 

@@ -72,6 +72,13 @@ hipError_t launch_paged_decode_append(const s4kv_shape& s, const void* q, const 
                                       const int32_t* block_table, const int32_t* ctx_lens,
                                       int32_t max_ctx, float sm_scale, void* out, void* workspace,
                                       hipStream_t stream);
+// The same with the workspace in the library's static per-device array
+// (S4KV_NOALLOC_SCRATCH_BYTES; the caller has checked the size).
+hipError_t launch_paged_decode_append_noalloc(const s4kv_shape& s, const void* q, const void* k_new,
+                                              const void* v_new, void* pages, void* tail_k,
+                                              void* tail_v, const int32_t* block_table,
+                                              const int32_t* ctx_lens, int32_t max_ctx,
+                                              float sm_scale, void* out, hipStream_t stream);
 hipError_t launch_paged_mq(const s4kv_shape& s, const void* q, const int32_t* cu_q, int32_t max_q,
                            int32_t total_q, const void* pages, const void* tail_k, const void* tail_v,
                            const int32_t* block_table, const int32_t* ctx_lens, int32_t max_ctx,

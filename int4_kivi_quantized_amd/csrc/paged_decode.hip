@@ -51,10 +51,17 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
 #include "page_quant.h"
+
+// The decode workspace of s4kv_paged_decode_append_noalloc, for callers that
+// cannot allocate: one copy of this array per device, held until the process
+// ends. Host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[S4KV_NOALLOC_SCRATCH_BYTES];
 
 namespace s4kv {
 namespace {
@@ -1485,6 +1492,43 @@ hipError_t launch_paged_mq(const s4kv_shape& s, const void* q, const int32_t* cu
                                             cu_q, gq, total_q, stream);
   if (e != hipSuccess) return e;
   return launch_merge(s, W, max_ctx, ws, ctx_lens, out, columns, cu_q, gq, total_q, stream);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  if (g_scratch_ptr[dev] == nullptr) return hipErrorInvalidSymbol;
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_paged_decode_append_noalloc(const s4kv_shape& s, const void* q, const void* k_new,
+                                              const void* v_new, void* pages, void* tail_k,
+                                              void* tail_v, const int32_t* block_table,
+                                              const int32_t* ctx_lens, int32_t max_ctx,
+                                              float sm_scale, void* out, hipStream_t stream) {
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_paged_decode_append(s, q, k_new, v_new, pages, tail_k, tail_v, block_table,
+                                    ctx_lens, max_ctx, sm_scale, out, ws, stream);
 }
 
 }  // namespace s4kv

@@ -30,6 +30,8 @@ S4KV_ERR_INVALID_ARG = 1
 S4KV_ERR_UNSUPPORTED = 2
 S4KV_ERR_WORKSPACE = 3
 S4KV_ERR_HIP = 4
+S4KV_ERR_SCRATCH_LIMIT = 5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class S4KVError(RuntimeError):
@@ -102,6 +104,9 @@ def load():
     lib.s4kv_paged_decode_append.argtypes = [SP, P, P, P, P, P, P, P, P, I32, ctypes.c_float, P,
                                              P, ctypes.c_size_t, P]
     lib.s4kv_paged_decode_append.restype = ctypes.c_int
+    lib.s4kv_paged_decode_append_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, I32,
+                                                     ctypes.c_float, P, P]
+    lib.s4kv_paged_decode_append_noalloc.restype = ctypes.c_int
     lib.s4kv_fp16_pool_bytes.argtypes = [SP]
     lib.s4kv_fp16_pool_bytes.restype = ctypes.c_size_t
     lib.s4kv_fp16_append.argtypes = [SP, P, P, P, P, I32, P, P, P]
@@ -137,7 +142,7 @@ def load():
 EXPORTED = (
     "s4kv_validate", "s4kv_status_string", "s4kv_pool_bytes", "s4kv_tail_bytes",
     "s4kv_quantize_append", "s4kv_decode_workspace_bytes", "s4kv_paged_decode",
-    "s4kv_paged_decode_append",
+    "s4kv_paged_decode_append", "s4kv_paged_decode_append_noalloc",
     "s4kv_fp16_pool_bytes", "s4kv_fp16_append", "s4kv_fp16_paged_decode",
     "s4kv_fp8_pool_bytes", "s4kv_fp8_append", "s4kv_fp8_paged_decode",
     "s4kv_mq_workspace_bytes", "s4kv_paged_attention_mq",
@@ -287,6 +292,27 @@ def s4kv_paged_decode_append(shape, q, k_new, v_new, pages, tail_k, tail_v, bloc
         int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "s4kv_paged_decode_append")
+
+
+def s4kv_paged_decode_append_noalloc(shape, q, k_new, v_new, pages, tail_k, tail_v, block_table,
+                                     ctx_lens, max_ctx, sm_scale, out, stream=None):
+    """s4kv_paged_decode_append with the decode workspace in the library's
+    static per-device array (no workspace argument, nothing allocated); see
+    s4kv.h."""
+    import torch
+    _check_q_out(shape, q, out)
+    _numel(k_new, shape.num_seqs * shape.num_kv_heads * HEAD_DIM, "k_new")
+    _numel(v_new, shape.num_seqs * shape.num_kv_heads * HEAD_DIM, "v_new")
+    _check_tables(shape, block_table, ctx_lens)
+    _numel(pages, s4kv_pool_bytes(shape), "pages", at_least=True)
+    _check_tails(shape, tail_k, tail_v)
+    st = load().s4kv_paged_decode_append_noalloc(
+        ctypes.byref(shape.c()), _ptr(q, torch.float16, "q"), _ptr(k_new, torch.float16, "k_new"),
+        _ptr(v_new, torch.float16, "v_new"), _ptr(pages, torch.uint8, "pages"),
+        _ptr(tail_k, torch.float16, "tail_k"), _ptr(tail_v, torch.float16, "tail_v"),
+        _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_lens, torch.int32, "ctx_lens"),
+        int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"), _stream(stream))
+    _check(st, "s4kv_paged_decode_append_noalloc")
 
 
 def s4kv_mq_workspace_bytes(shape, max_ctx, max_q):

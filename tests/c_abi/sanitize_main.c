@@ -49,7 +49,9 @@ int main(void) {
   CHECK(s4kv_fp16_paged_decode(&s, P, P, IP, IP, 1000, 0.088f, P, P, ws, NULL) == S4KV_OK);
   CHECK(s4kv_fp8_append(&s, P, P, IP, IP, 16, IP, FP, FP, P, NULL) == S4KV_OK);
   CHECK(s4kv_fp8_paged_decode(&s, P, P, IP, IP, 1000, 0.088f, FP, FP, P, P, ws, NULL) == S4KV_OK);
-  CHECK(launched(n) == 10);
+  CHECK(s4kv_paged_decode_append_noalloc(&s, P, P, P, P, P, P, IP, IP, 1000, 0.088f, P, NULL) ==
+        S4KV_OK);
+  CHECK(launched(n) == 11);
   /* max_new 0 appends nothing and launches nothing */
   n = stub_launches();
   CHECK(s4kv_quantize_append(&s, P, P, IP, IP, 0, IP, P, P, P, NULL) == S4KV_OK);
@@ -81,6 +83,16 @@ int main(void) {
                                 NULL) == S4KV_ERR_WORKSPACE);
   CHECK(s4kv_fp8_append(&s, P, P, IP, IP, 16, IP, NULL, FP, P, NULL) == S4KV_ERR_INVALID_ARG);
   CHECK(s4kv_fp16_paged_decode(&s, P, P, IP, IP, 1000, 0.088f, P, P, 0, NULL) == S4KV_ERR_WORKSPACE);
+  CHECK(s4kv_paged_decode_append_noalloc(&s, NULL, P, P, P, P, P, IP, IP, 1000, 0.088f, P, NULL) ==
+        S4KV_ERR_INVALID_ARG);
+  {
+    /* a shape whose workspace exceeds the static scratch array */
+    const s4kv_shape wide = {65535, 16, 16, S4KV_HEAD_DIM, S4KV_PAGE_SIZE, 100, 64};
+    CHECK(s4kv_validate(&wide) == S4KV_OK);
+    CHECK(s4kv_decode_workspace_bytes(&wide, 1000) > (size_t)S4KV_NOALLOC_SCRATCH_BYTES);
+    CHECK(s4kv_paged_decode_append_noalloc(&wide, P, P, P, P, P, P, IP, IP, 1000, 0.088f, P,
+                                           NULL) == S4KV_ERR_SCRATCH_LIMIT);
+  }
   CHECK(launched(n) == 0);
 
   /* shapes at and past the limits: validation arithmetic must not overflow */

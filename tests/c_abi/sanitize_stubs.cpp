@@ -30,6 +30,12 @@ hipError_t launch_paged_decode_append(const s4kv_shape&, const void*, const void
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_paged_decode_append_noalloc(const s4kv_shape&, const void*, const void*,
+                                              const void*, void*, void*, void*, const int32_t*,
+                                              const int32_t*, int32_t, float, void*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_paged_mq(const s4kv_shape&, const void*, const int32_t*, int32_t, int32_t,
                            const void*, const void*, const void*, const int32_t*, const int32_t*,
                            int32_t, float, void*, void*, hipStream_t) {
