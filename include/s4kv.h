@@ -283,10 +283,17 @@ s4kv_status s4kv_kivi2_paged_decode(const s4kv_shape* shape, const void* q, cons
  * attends causally:
  *   O[row][j] = sum_{s <= p} softmax_s(sm_scale * q[row][j] . k_s) v_s,
  *   row = cu_q[b] + t, KV head of j = j / (Hq/Hkv).
- * One launch serves every sequence; max_q * (Hq / Hkv) <= 16. */
+ * One launch serves every sequence. The (token, query head) pairs of a KV
+ * head feed the matrix cores as columns, 16 at a time: with max_q * Hq / Hkv
+ * <= 16 (speculative verify) one pass over the pages serves all of a
+ * sequence's tokens; with more (a prefill chunk) the tokens are cut into
+ * tiles of floor(16 / (Hq / Hkv)) whole tokens, each tile streaming the
+ * pages up to its last token's position. Limits: num_seqs * tiles <= 65535
+ * and num_seqs * tiles * Hkv * (max_pages_per_seq + 1) < 2^31, tiles =
+ * ceil(max_q / tile tokens). */
 
 /* Bytes of device workspace s4kv_paged_attention_mq needs (0 if the shape is
- * invalid, max_ctx < 1, max_q < 1 or max_q * Hq / Hkv > 16). */
+ * invalid, max_ctx < 1, max_q < 1 or the tiles exceed the limits above). */
 size_t s4kv_mq_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx, int32_t max_q);
 
 /* Multi-query attention step.
@@ -303,8 +310,8 @@ size_t s4kv_mq_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx, int32_t
  *   workspace    device scratch of at least s4kv_mq_workspace_bytes.
  * Device preconditions: as s4kv_paged_decode, plus 1 <= T_b <= min(max_q,
  * ctx_lens[b]) and cu_q as above.
- * Returns S4KV_OK; S4KV_ERR_INVALID_ARG / S4KV_ERR_UNSUPPORTED (max_q *
- * Hq / Hkv > 16) / S4KV_ERR_WORKSPACE before any launch; S4KV_ERR_HIP if a
+ * Returns S4KV_OK; S4KV_ERR_INVALID_ARG / S4KV_ERR_UNSUPPORTED (tiles beyond
+ * the limits above) / S4KV_ERR_WORKSPACE before any launch; S4KV_ERR_HIP if a
  * launch fails. */
 s4kv_status s4kv_paged_attention_mq(const s4kv_shape* shape, const void* q, const int32_t* cu_q,
                                     int32_t max_q, int32_t total_q, const void* pages,

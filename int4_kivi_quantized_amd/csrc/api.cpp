@@ -182,7 +182,7 @@ s4kv_status s4kv_kivi2_paged_decode(const s4kv_shape* shape, const void* q, cons
 
 size_t s4kv_mq_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx, int32_t max_q) {
   if (check_shape(shape) != S4KV_OK || max_ctx < 1 || max_q < 1) return 0;
-  if ((int64_t)max_q * (shape->num_q_heads / shape->num_kv_heads) > S4KV_MAX_GROUP) return 0;
+  if (!s4kv::mq_tiling_fits(*shape, s4kv::mq_tiling(*shape, max_q))) return 0;
   return s4kv::mq_workspace_bytes(*shape, max_q);
 }
 
@@ -197,8 +197,7 @@ s4kv_status s4kv_paged_attention_mq(const s4kv_shape* shape, const void* q, cons
   if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)shape->max_pages_per_seq * S4KV_PAGE_SIZE)
     return S4KV_ERR_INVALID_ARG;
   if (max_q < 1 || total_q < 1) return S4KV_ERR_INVALID_ARG;
-  if ((int64_t)max_q * (shape->num_q_heads / shape->num_kv_heads) > S4KV_MAX_GROUP)
-    return S4KV_ERR_UNSUPPORTED;
+  if (!s4kv::mq_tiling_fits(*shape, s4kv::mq_tiling(*shape, max_q))) return S4KV_ERR_UNSUPPORTED;
   // query rows times heads must index in int64 without overflow of int32 row counts
   if ((int64_t)total_q > (int64_t)shape->num_seqs * max_q) return S4KV_ERR_INVALID_ARG;
   if (!q || !cu_q || !pages || !tail_k || !tail_v || !block_table || !ctx_lens || !out || !workspace)

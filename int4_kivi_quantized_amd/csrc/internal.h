@@ -63,7 +63,36 @@ hipError_t launch_quantize_append(const s4kv_shape& s, const void* k, const void
                                   void* tail_v, hipStream_t stream, int bits = 4);
 
 // Multi-query attention over the int4 cache: up to max_q query tokens per
-// sequence (max_q * Hq / Hkv <= 16), causal within the sequence.
+// sequence, causal within the sequence. The (token, head) columns of a
+// sequence go to the matrix cores in tiles of at most 16 columns (tpt whole
+// tokens each); with more than one tile per sequence every tile is streamed
+// as a virtual sequence of its own (ct_n tiles per sequence).
+struct MqTiling {
+  int32_t tpt;           // tokens per tile
+  int32_t ct_n;          // tiles per sequence
+  int32_t columns;       // columns per tile, tpt * Hq / Hkv
+  int64_t virtual_seqs;  // num_seqs * ct_n
+};
+inline MqTiling mq_tiling(const s4kv_shape& s, int32_t max_q) {
+  const int gq = s.num_q_heads / s.num_kv_heads;
+  MqTiling t;
+  if ((int64_t)max_q * gq <= kMaxGroup) {
+    t.tpt = max_q;
+    t.ct_n = 1;
+  } else {
+    t.tpt = kMaxGroup / gq;  // whole tokens per tile of at most 16 columns
+    t.ct_n = static_cast<int32_t>(((int64_t)max_q + t.tpt - 1) / t.tpt);
+  }
+  t.columns = t.tpt * gq;
+  t.virtual_seqs = (int64_t)s.num_seqs * t.ct_n;
+  return t;
+}
+// Whether the tiles fit the launch limits: at most 65535 virtual sequences
+// (the merge grid's y dimension) and a flat unit count that fits in int32.
+inline bool mq_tiling_fits(const s4kv_shape& s, const MqTiling& t) {
+  return t.virtual_seqs <= 65535 &&
+         t.virtual_seqs * s.num_kv_heads * ((int64_t)s.max_pages_per_seq + 1) <= INT32_MAX;
+}
 size_t mq_workspace_bytes(const s4kv_shape& s, int32_t max_q);
 // Append one token per sequence (position ctx_lens[b] - 1, from k_new /
 // v_new [B][Hkv][128]) and decode, in one launch of the decode stream.

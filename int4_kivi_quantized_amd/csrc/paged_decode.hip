@@ -513,6 +513,31 @@ __device__ inline int units_of(int ctx, int max_pages) {
   return ctx / kPage + ((ctx % kPage) ? 1 : 0);
 }
 
+// Multi-query column tiles: when a sequence's new tokens need more than 16
+// matrix-core columns per KV head, they are cut into tiles of tpt whole
+// tokens, and tile k of sequence b is streamed as its own virtual sequence
+// bv = b * ct_n + k. Its columns are tokens [k tpt, k tpt + tpt) of b's
+// new tokens, which see the cache positions up to the tile's last token, so
+// the tile needs only the pages (and the tail, if it reaches it) holding
+// those positions; a tile past the sequence's token count has no units.
+// Returns the full pages and tail tokens the virtual sequence streams.
+struct VSpan {
+  int full, tail;
+};
+__device__ inline VSpan tile_span(int bv, const int32_t* ctx_lens, int max_pages,
+                                  const int32_t* cu_q, int ct_n, int tpt) {
+  const int b = bv / ct_n;
+  const int ctx = min(ctx_lens[b], max_pages * kPage);
+  if (ctx <= 0) return {0, 0};
+  const int tb = cu_q[b + 1] - cu_q[b];
+  const int t0 = (bv - b * ct_n) * tpt;
+  if (t0 >= tb) return {0, 0};
+  const int len = min(ctx, max(1, ctx - tb + min(tb, t0 + tpt)));  // positions 0 .. len - 1
+  const int full = ctx / kPage;
+  if (len <= full * kPage) return {(len + kPage - 1) / kPage, 0};
+  return {full, ctx % kPage};
+}
+
 // The wave that owns unit u when U units are split into W ranges
 // [w*U/W, (w+1)*U/W): the largest w with floor(w*U/W) <= u.
 __device__ __host__ inline int owner_wave(int64_t u, int64_t U, int W) {
@@ -545,7 +570,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
     int32_t* __restrict__ total_units, int2* __restrict__ seg_waves, int32_t B, int32_t max_pages,
     int32_t hkv, float sm_scale, float* __restrict__ slots, const int32_t* __restrict__ cu_q,
-    int32_t gq, int32_t total_q, const __half* __restrict__ k_new, const __half* __restrict__ v_new) {
+    int32_t gq, int32_t total_q, const __half* __restrict__ k_new, const __half* __restrict__ v_new,
+    int32_t ct_n, int32_t tpt) {
   static_assert(!kAppend || (kBits == 4 && !kMQ), "the fused append serves the int4 decode");
   constexpr bool kPacked = (G <= 8);    // columns split between the two pages of a pair
   constexpr bool kHiLoCols = (G <= 4);  // and between the hi / lo parts of the output operand
@@ -557,6 +583,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   constexpr int kStages = PF::kStages;
   using PStage = std::conditional_t<kBits == 4, PackedStage, PackedStage2>;
   using WStage = std::conditional_t<kBits == 4, WideStage, WideStage2>;
+  // kMQ: B counts virtual sequences (column tiles, see tile_span); the real
+  // sequence of virtual sequence b is b / ct_n
+  auto span_of = [&](int b) -> VSpan {
+    if constexpr (kMQ) {
+      return tile_span(b, ctx_lens, max_pages, cu_q, ct_n, tpt);
+    } else {
+      const int ctx = min(ctx_lens[b], max_pages * kPage);
+      return ctx > 0 ? VSpan{ctx / kPage, ctx % kPage} : VSpan{0, 0};
+    }
+  };
+  auto nunits_of = [&](int b) {
+    const VSpan v = span_of(b);
+    return v.full + (v.tail ? 1 : 0);
+  };
+  auto real_seq = [&](int b) { return kMQ ? b / ct_n : b; };
 
   // ---- unit plan ----
   // units(b) = full pages of b plus one for a non-empty tail; (b, h) pairs are
@@ -566,7 +607,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   int64_t U;
   {
     int local = 0;
-    for (int b = lane; b < B; b += 64) local += units_of(ctx_lens[b], max_pages);
+    for (int b = lane; b < B; b += 64) local += nunits_of(b);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
     // every lane holds the sum; readfirstlane tells the compiler it is
@@ -589,7 +630,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     int64_t carry = 0;
     for (int k = 0; k < nchunks && b0 < 0; ++k) {
       const int b = 64 * k + lane;
-      const int n = (b < B) ? units_of(ctx_lens[b], max_pages) : 0;
+      const int n = (b < B) ? nunits_of(b) : 0;
       int incl = n;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -634,9 +675,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     int tail;    // tokens in the fp16 tail of b
   };
   auto seq_info = [&](int b, Cursor& cu) {
-    const int ctx = min(ctx_lens[b], max_pages * kPage);
-    cu.full = ctx > 0 ? ctx / kPage : 0;
-    cu.tail = ctx > 0 ? ctx % kPage : 0;
+    const VSpan v = span_of(b);
+    cu.full = v.full;
+    cu.tail = v.tail;
     cu.nunits = cu.full + (cu.tail ? 1 : 0);
   };
   Cursor start;
@@ -677,17 +718,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   int pstage = 0, cstage = 0;  // ring slots of the next issue / the next consume
   // kMQ: the column's causal limit (cache position) in the current segment
   int col_lim = 0;
-  auto q_row = [&](int b, int h, int ctx) {
+  auto q_row = [&](int bv, int h) {
     if constexpr (kMQ) {
       // a sequence with fewer new tokens than columns repeats its last token
       // in the spare columns (their results are not stored)
+      const int b = real_seq(bv);
+      const int ctx = min(ctx_lens[b], max_pages * kPage);
       const int q0 = cu_q[b], tb = cu_q[b + 1] - q0;
-      const int t = min(head / gq, max(tb - 1, 0));
+      const int t = min((bv - b * ct_n) * tpt + head / gq, max(tb - 1, 0));
       col_lim = ctx - tb + t;
       const int64_t row = min(max((int64_t)q0 + t, (int64_t)0), (int64_t)total_q - 1);
       return reinterpret_cast<const uint8_t*>(q + (row * hq + h * gq + head % gq) * kHeadDim);
     } else {
-      return reinterpret_cast<const uint8_t*>(q + ((int64_t)b * hq + h * G + head) * kHeadDim);
+      return reinterpret_cast<const uint8_t*>(q + ((int64_t)bv * hq + h * G + head) * kHeadDim);
     }
   };
   // Block ids of the pair at the producer cursor, loaded one pair ahead of
@@ -705,7 +748,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     // Both ids load unconditionally (the second index clamped to the row) and
     // the pair / single choice is made where they are used, one pair later,
     // so nothing waits for these scalar loads here.
-    const int32_t* row = block_table + prod.b * max_pages;
+    const int32_t* row = block_table + real_seq(prod.b) * max_pages;
     nid_a = row[prod.unit];
     nid_b = row[min(prod.unit + 1, max_pages - 1)];
   };
@@ -787,7 +830,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     // the query of the new (b, h); loading it waits for the ring's DMAs,
     // once per segment
     u4 raw[4];
-    const uint8_t* qr = q_row(b, h, cu.full * kPage + cu.tail);
+    const uint8_t* qr = q_row(b, h);
 #pragma unroll
     for (int m = 0; m < 4; ++m) raw[m] = ld16(qr + 2 * (32 * m + 8 * g));
     // the column's pre-scale 2^E: E = kQExp - e with max_d |q_d| = f 2^e,
@@ -927,7 +970,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   // in packed layouts only page-A columns take it
   // tail_pos0: cache position of the tail's first token
   auto process_tail = [&](int tail_n, int tail_pos0) {
-    const int64_t bh = (int64_t)cur_b * hkv + cur_h;
+    const int64_t bh = (int64_t)real_seq(cur_b) * hkv + cur_h;
     const uint8_t* tk = reinterpret_cast<const uint8_t*>(tail_k + bh * kPage * kHeadDim);
     const uint8_t* tv = reinterpret_cast<const uint8_t*>(tail_v + bh * kPage * kHeadDim);
     // kAppend: the new token is tail slot tail_n - 1; it is read from the
@@ -1245,80 +1288,98 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
 // Merge, for (sequence b, KV head h), the partial results of the waves whose
 // unit ranges touched (b, h) (recorded by the wave owning its first unit): m in
 // log2 units, O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M the
-// max over the slots s. The block is R slot groups x (G heads x 32 output
-// quads): each thread merges every R-th slot of its quad online, then the R
-// partial merges of a quad combine through LDS.
-// With cu_q (several query tokens per sequence) the G columns of a slot are
-// (token, head) pairs, column jj = token jj / gq, head jj % gq; columns past
-// the sequence's token count are merged but not stored.
+// max over the slots s. A block serves hb heads of one (b, h): hb x R slot
+// groups x 32 output quads. Thread group r merges slots r, r + R, ... online
+// (one slot each when R covers them, as the launch sizes it); the groups'
+// maxima meet in LDS, each group rescales to the common maximum, and the R
+// groups add up in a fixed binary tree (same order every call).
+// With cu_q (several query tokens per sequence) blockIdx.y is a virtual
+// sequence, column tile bv % ct_n of sequence bv / ct_n (see tile_span), and
+// the G columns of a slot are (token, head) pairs, column jj = token
+// tile * tpt + jj / gq, head jj % gq; columns past the sequence's token count
+// are merged but not stored.
 constexpr int kReduceThreads = 1024;
 __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
     const float* __restrict__ slots, const int32_t* __restrict__ total_units,
     const int2* __restrict__ seg_waves, const int32_t* __restrict__ ctx_lens, int32_t max_pages,
     int32_t hkv, int32_t G, int32_t W, __half* __restrict__ out, const int32_t* __restrict__ cu_q,
-    int32_t gq, int32_t total_q) {
-  __shared__ float red_m[kReduceThreads], red_l[kReduceThreads];
+    int32_t gq, int32_t total_q, int32_t hb, int32_t R, int32_t ct_n, int32_t tpt) {
+  __shared__ float red_m[kReduceThreads / 32], red_l[kReduceThreads / 32];
   __shared__ f4 red_o[kReduceThreads];
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int C = 32 * G;
-  const int R = blockDim.x / C;
+  const int groups = (G + hb - 1) / hb;
+  const int h = blockIdx.x / groups, b = blockIdx.y;
   const int t = threadIdx.x;
-  const int combo = t % C, r = t / C;
-  const int jj = combo >> 5, d0 = 4 * (combo & 31);
-  __half* o;
-  bool store = true;
+  const int q = t & 31, rg = t >> 5;        // output quad; (head, slot group) index
+  const int r = rg % R, jb = rg / R;
+  const int jj = (blockIdx.x % groups) * hb + jb;
+  const int d0 = 4 * q;
+  const bool live = jj < G;
+  __half* o = nullptr;
+  bool store = live;
+  int n = 0;
   if (cu_q != nullptr) {
-    const int q0 = cu_q[b], tq = jj / gq;
+    const int bs = b / ct_n;
+    const int q0 = cu_q[bs], tq = (b - bs * ct_n) * tpt + (live ? jj : 0) / gq;
     // rows outside [0, total_q) are never written, whatever cu_q holds
-    store = tq < cu_q[b + 1] - q0 && q0 >= 0 && (int64_t)q0 + tq < total_q;
+    store = live && tq < cu_q[bs + 1] - q0 && q0 >= 0 && (int64_t)q0 + tq < total_q;
     o = out + (((int64_t)q0 + tq) * hkv * gq + h * gq + jj % gq) * kHeadDim + d0;
+    const VSpan v = tile_span(b, ctx_lens, max_pages, cu_q, ct_n, tpt);
+    n = v.full + (v.tail ? 1 : 0);
   } else {
+    n = units_of(ctx_lens[b], max_pages);
     o = out + ((int64_t)b * hkv * G + h * G + jj) * kHeadDim + d0;
   }
   const int64_t bh = (int64_t)b * hkv + h;
-  const int n = units_of(ctx_lens[b], max_pages);
   const int64_t U = total_units[0];
-  const int2 ws = seg_waves[bh];
   if (n <= 0 || U <= 0) {
     if (r == 0 && store) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
     return;
   }
+  const int2 ws = seg_waves[bh];
   float M = kNegInf, L = 0.f;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int wv = ws.x + r; wv <= ws.y; wv += R) {
-    // waves strictly between two owners can have empty ranges (when U < W);
-    // they wrote nothing
-    if ((int64_t)wv * U / W == (int64_t)(wv + 1) * U / W) continue;
-    const float* sl = slots + ((bh + wv) * G + jj) * kSlotStride;
-    const float ms = sl[kHeadDim], ls = sl[kHeadDim + 1];
-    const f4 os = *reinterpret_cast<const f4*>(sl + d0);
-    if (ms == kNegInf) continue;
-    const float Mn = fmaxf(M, ms);
-    const float a = (M == kNegInf) ? 0.f : exp2f(M - Mn);
-    const float c = exp2f(ms - Mn);
-    L = L * a + ls * c;
-    acc = acc * a + os * c;
-    M = Mn;
-  }
-  if (R > 1) {
-    red_m[t] = M;
-    red_l[t] = L;
-    red_o[t] = acc;
-    __syncthreads();
-    if (r != 0) return;
-    for (int k = 1; k < R; ++k) {
-      const float ms = red_m[t + k * C];
+  if (live) {
+    for (int wv = ws.x + r; wv <= ws.y; wv += R) {
+      // waves strictly between two owners can have empty ranges (when U < W);
+      // they wrote nothing
+      if ((int64_t)wv * U / W == (int64_t)(wv + 1) * U / W) continue;
+      const float* sl = slots + ((bh + wv) * G + jj) * kSlotStride;
+      const float ms = sl[kHeadDim], ls = sl[kHeadDim + 1];
+      const f4 os = *reinterpret_cast<const f4*>(sl + d0);
       if (ms == kNegInf) continue;
       const float Mn = fmaxf(M, ms);
       const float a = (M == kNegInf) ? 0.f : exp2f(M - Mn);
       const float c = exp2f(ms - Mn);
-      L = L * a + red_l[t + k * C] * c;
-      acc = acc * a + red_o[t + k * C] * c;
+      L = L * a + ls * c;
+      acc = acc * a + os * c;
       M = Mn;
     }
   }
-  if (!store) return;
+  if (R > 1) {
+    if (q == 0) red_m[rg] = M;
+    __syncthreads();
+    float Mh = kNegInf;
+    for (int k = 0; k < R; ++k) Mh = fmaxf(Mh, red_m[jb * R + k]);
+    const float a = (M == kNegInf) ? 0.f : exp2f(M - Mh);
+    acc = acc * a;
+    L *= a;
+    red_o[t] = acc;
+    if (q == 0) red_l[rg] = L;
+    __syncthreads();
+    for (int stride = R / 2; stride > 0; stride /= 2) {
+      if (r < stride) {
+        acc += red_o[t + 32 * stride];
+        red_o[t] = acc;
+        if (q == 0) {
+          L += red_l[rg + stride];
+          red_l[rg] = L;
+        }
+      }
+      __syncthreads();
+    }
+    L = red_l[jb * R];
+  }
+  if (r != 0 || !store) return;
   const float inv = 1.0f / L;
   __half2 lo = __floats2half2_rn(acc[0] * inv, acc[1] * inv);
   __half2 hi = __floats2half2_rn(acc[2] * inv, acc[3] * inv);
@@ -1335,14 +1396,16 @@ hipError_t launch_g(const s4kv_shape& s, int W, const void* q, const void* pages
                     const void* tail_k, const void* tail_v, const int32_t* block_table,
                     const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves, float sm_scale,
                     float* slots, const int32_t* cu_q, int32_t gq, int32_t total_q,
-                    const void* k_new, const void* v_new, hipStream_t stream) {
+                    const void* k_new, const void* v_new, hipStream_t stream, int32_t ct_n,
+                    int32_t tpt) {
   hipLaunchKernelGGL((decode_stream_kernel<G, kMQ, kBits, kAppend>), dim3(W), dim3(64), 0, stream,
                      static_cast<const __half*>(q), static_cast<uint8_t*>(const_cast<void*>(pages)),
                      static_cast<__half*>(const_cast<void*>(tail_k)),
                      static_cast<__half*>(const_cast<void*>(tail_v)),
                      block_table, ctx_lens, total_units, seg_waves, s.num_seqs, s.max_pages_per_seq,
                      s.num_kv_heads, sm_scale, slots, cu_q, gq, total_q,
-                     static_cast<const __half*>(k_new), static_cast<const __half*>(v_new));
+                     static_cast<const __half*>(k_new), static_cast<const __half*>(v_new), ct_n,
+                     tpt);
   return hipGetLastError();
 }
 
@@ -1353,13 +1416,13 @@ hipError_t launch_columns(int G, const s4kv_shape& s, int W, const void* q, cons
                           const int32_t* ctx_lens, int32_t* total_units, int2* seg_waves,
                           float sm_scale, float* slots, const int32_t* cu_q, int32_t gq,
                           int32_t total_q, hipStream_t stream, const void* k_new = nullptr,
-                          const void* v_new = nullptr) {
+                          const void* v_new = nullptr, int32_t ct_n = 1, int32_t tpt = 1) {
   switch (G) {
 #define S4KV_CASE(g)                                                                             \
   case g:                                                                                        \
     return launch_g<g, kMQ, kBits, kAppend>(s, W, q, pages, tail_k, tail_v, block_table,         \
                                             ctx_lens, total_units, seg_waves, sm_scale, slots,  \
-                                            cu_q, gq, total_q, k_new, v_new, stream);
+                                            cu_q, gq, total_q, k_new, v_new, stream, ct_n, tpt);
     S4KV_CASE(1) S4KV_CASE(2) S4KV_CASE(3) S4KV_CASE(4) S4KV_CASE(5) S4KV_CASE(6) S4KV_CASE(7)
     S4KV_CASE(8) S4KV_CASE(9) S4KV_CASE(10) S4KV_CASE(11) S4KV_CASE(12) S4KV_CASE(13)
     S4KV_CASE(14) S4KV_CASE(15) S4KV_CASE(16)
@@ -1404,20 +1467,24 @@ SplitWorkspace split_workspace(const s4kv_shape& s, void* workspace) {
 namespace {
 hipError_t launch_merge(const s4kv_shape& s, int W, int32_t max_ctx, const SplitWorkspace& ws,
                         const int32_t* ctx_lens, void* out, int G, const int32_t* cu_q, int32_t gq,
-                        int32_t total_q, hipStream_t stream) {
-  // Slot groups per (sequence, head): about the number of waves that share a
-  // (b, h) when every context is max_ctx long (W waves over B * Hkv * pages
-  // units), rounded up to a power of two and capped by the block size. This
-  // only sizes the launch; any count of sharing waves is merged correctly.
-  const int C = 32 * G;
+                        int32_t total_q, hipStream_t stream, int32_t ct_n = 1, int32_t tpt = 1) {
+  // Slot groups per (sequence, head): the number of waves that share a (b, h)
+  // when every context is max_ctx long (W waves over B * Hkv * pages units),
+  // rounded up to a power of two, at most 32. Heads per block: as many as fit
+  // 1024 threads next to the R groups. This only sizes the launch; any count
+  // of sharing waves is merged correctly.
   const int64_t per_bh = ((int64_t)max_ctx + kPage - 1) / kPage;
   const int64_t units = (int64_t)s.num_seqs * s.num_kv_heads * per_bh;
-  const int64_t share = (int64_t)W * per_bh / (units > 0 ? units : 1) + 2;
+  const int64_t share = ((int64_t)W * per_bh + units - 1) / (units > 0 ? units : 1);
   int R = 1;
-  while (R < share && 2 * R * C <= kReduceThreads) R *= 2;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads, s.num_seqs), dim3(C * R), 0,
-                     stream, ws.slots, ws.total_units, reinterpret_cast<const int2*>(ws.seg_waves), ctx_lens, s.max_pages_per_seq,
-                     s.num_kv_heads, G, W, static_cast<__half*>(out), cu_q, gq, total_q);
+  while (R < share && R < 32) R *= 2;
+  const int hb = std::max(1, std::min(G, kReduceThreads / (32 * R)));
+  const int groups = (G + hb - 1) / hb;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads * groups, s.num_seqs),
+                     dim3(32 * R * hb), 0, stream, ws.slots, ws.total_units,
+                     reinterpret_cast<const int2*>(ws.seg_waves), ctx_lens, s.max_pages_per_seq,
+                     s.num_kv_heads, G, W, static_cast<__half*>(out), cu_q, gq, total_q, hb, R,
+                     ct_n, tpt);
   return hipGetLastError();
 }
 size_t workspace_for_columns(const s4kv_shape& s, int columns) {
@@ -1437,7 +1504,10 @@ size_t workspace_bytes(const s4kv_shape& s) {
 }
 
 size_t mq_workspace_bytes(const s4kv_shape& s, int32_t max_q) {
-  return workspace_for_columns(s, max_q * (s.num_q_heads / s.num_kv_heads));
+  const MqTiling t = mq_tiling(s, max_q);
+  s4kv_shape sv = s;
+  sv.num_seqs = static_cast<int32_t>(t.virtual_seqs);
+  return workspace_for_columns(sv, t.columns);
 }
 
 hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* pages,
@@ -1482,16 +1552,20 @@ hipError_t launch_paged_mq(const s4kv_shape& s, const void* q, const int32_t* cu
                            int32_t total_q, const void* pages, const void* tail_k, const void* tail_v,
                            const int32_t* block_table, const int32_t* ctx_lens, int32_t max_ctx,
                            float sm_scale, void* out, void* workspace, hipStream_t stream) {
-  const SplitWorkspace ws = split_workspace(s, workspace);
+  // the stream and the merge run over virtual sequences, one per column tile
+  const MqTiling t = mq_tiling(s, max_q);
+  s4kv_shape sv = s;
+  sv.num_seqs = static_cast<int32_t>(t.virtual_seqs);
+  const SplitWorkspace ws = split_workspace(sv, workspace);
   const int W = resident_waves();
   const int gq = s.num_q_heads / s.num_kv_heads;
-  const int columns = max_q * gq;
-  const hipError_t e = launch_columns<true, 4>(columns, s, W, q, pages, tail_k, tail_v, block_table,
-                                            ctx_lens, ws.total_units,
-                                            reinterpret_cast<int2*>(ws.seg_waves), sm_scale, ws.slots,
-                                            cu_q, gq, total_q, stream);
+  const hipError_t e = launch_columns<true, 4>(
+      t.columns, sv, W, q, pages, tail_k, tail_v, block_table, ctx_lens, ws.total_units,
+      reinterpret_cast<int2*>(ws.seg_waves), sm_scale, ws.slots, cu_q, gq, total_q, stream,
+      nullptr, nullptr, t.ct_n, t.tpt);
   if (e != hipSuccess) return e;
-  return launch_merge(s, W, max_ctx, ws, ctx_lens, out, columns, cu_q, gq, total_q, stream);
+  return launch_merge(sv, W, max_ctx, ws, ctx_lens, out, t.columns, cu_q, gq, total_q, stream,
+                      t.ct_n, t.tpt);
 }
 
 // Device address of `scratch` on the current device, looked up once per

@@ -28,7 +28,8 @@ int main(void) {
   CHECK(s4kv_tail_bytes(&s) == (size_t)4 * 8 * 16 * 128 * 2);
   CHECK(s4kv_decode_workspace_bytes(&s, 1000) > 0);
   CHECK(s4kv_mq_workspace_bytes(&s, 1000, 4) > s4kv_decode_workspace_bytes(&s, 1000));
-  CHECK(s4kv_mq_workspace_bytes(&s, 1000, 5) == 0);
+  CHECK(s4kv_mq_workspace_bytes(&s, 1000, 5) > s4kv_mq_workspace_bytes(&s, 1000, 4));
+  CHECK(s4kv_mq_workspace_bytes(&s, 1000, 70000) == 0);
 
   s4kv_shape bad = s;
   bad.head_dim = 96;

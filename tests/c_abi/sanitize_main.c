@@ -75,8 +75,8 @@ int main(void) {
         S4KV_ERR_INVALID_ARG);
   CHECK(s4kv_paged_decode_append(&s, P, P, P, P, P, P, IP, IP, 1000, 0.088f, P, P, ws - 1, NULL) ==
         S4KV_ERR_WORKSPACE);
-  CHECK(s4kv_paged_attention_mq(&s, P, IP, 5, 16, P, P, P, IP, IP, 1000, 0.088f, P, P, mws, NULL) ==
-        S4KV_ERR_UNSUPPORTED);
+  CHECK(s4kv_paged_attention_mq(&s, P, IP, 70000, 16, P, P, P, IP, IP, 1000, 0.088f, P, P, mws,
+                                NULL) == S4KV_ERR_UNSUPPORTED);
   CHECK(s4kv_paged_attention_mq(&s, P, IP, 4, 17, P, P, P, IP, IP, 1000, 0.088f, P, P, mws, NULL) ==
         S4KV_ERR_INVALID_ARG);
   CHECK(s4kv_paged_attention_mq(&s, P, IP, 4, 16, P, P, P, IP, IP, 1000, 0.088f, P, P, mws - 1,

@@ -16,7 +16,7 @@ size_t workspace_bytes(const s4kv_shape& s) {
   return 4096 + (size_t)s.num_seqs * s.num_kv_heads * 64;
 }
 size_t mq_workspace_bytes(const s4kv_shape& s, int32_t max_q) {
-  return workspace_bytes(s) * (size_t)max_q;
+  return workspace_bytes(s) * (size_t)mq_tiling(s, max_q).ct_n * 2;
 }
 hipError_t launch_quantize_append(const s4kv_shape&, const void*, const void*, const int32_t*,
                                   const int32_t*, int32_t, const int32_t*, void*, void*, void*,

@@ -287,7 +287,10 @@ def test_mq_workspace_and_refusals():
     w1 = s4kv.s4kv_mq_workspace_bytes(sh, 1000, 1)
     assert w1 == s4kv.s4kv_decode_workspace_bytes(sh, 1000)   # one token: the decode workspace
     assert s4kv.s4kv_mq_workspace_bytes(sh, 1000, 4) > w1
-    assert s4kv.s4kv_mq_workspace_bytes(sh, 1000, 5) == 0     # 5 x 4 columns > 16
+    # 5 tokens x 4 heads: two column tiles, twice the virtual sequences
+    assert s4kv.s4kv_mq_workspace_bytes(sh, 1000, 5) > s4kv.s4kv_mq_workspace_bytes(sh, 1000, 4)
+    # 70000 tokens in tiles of 4: more than 65535 virtual sequences
+    assert s4kv.s4kv_mq_workspace_bytes(sh, 1000, 70000) == 0
     assert s4kv.s4kv_mq_workspace_bytes(sh, 1000, 0) == 0
     assert s4kv.s4kv_mq_workspace_bytes(sh, 0, 1) == 0
     lib, P, fake = _raw_calls()
@@ -303,7 +306,8 @@ def test_mq_workspace_and_refusals():
                                            bt, cl, max_ctx, ctypes.c_float(0.088), out, wsp, ws_bytes,
                                            None)
 
-    assert call(max_q=5) == s4kv.S4KV_ERR_UNSUPPORTED
+    assert call(max_q=5) == s4kv.S4KV_ERR_WORKSPACE              # two tiles need more
+    assert call(max_q=70000) == s4kv.S4KV_ERR_UNSUPPORTED
     assert call(max_q=0) == s4kv.S4KV_ERR_INVALID_ARG
     assert call(total_q=0) == s4kv.S4KV_ERR_INVALID_ARG
     assert call(total_q=4 * 4 + 1) == s4kv.S4KV_ERR_INVALID_ARG     # more rows than B * max_q

@@ -5,7 +5,9 @@ attend causally over the dequantized pages and the fp16 tail. The reference is
 the oracle's multiquery_attention over the oracle's dequantized cache; the bar
 is the decode bar (2e-3 max-abs, 1e-3 relative L2). Ragged token counts,
 causal limits inside full pages, across page boundaries and inside the tail,
-and every column count up to 16 are covered.
+and every column count up to 16 are covered; so are token counts that need
+more than 16 matrix-core columns per KV head (streamed as column tiles), up
+to whole causal prefill chunks.
 """
 
 import numpy as np
@@ -114,3 +116,68 @@ def test_mq_full_size_sampled(name, max_q):
     if len(case.plan.sharing):
         seqs.add(int(case.plan.sharing[0]))
     _check(case, sorted(seqs), q, cu, out)
+
+
+@pytest.mark.parametrize("g,max_q", [(1, 40), (3, 64), (4, 64), (8, 33), (16, 9)])
+def test_mq_wide_tiles(g, max_q):
+    """More tokens per sequence than 16 / G: the columns go out in tiles of
+    whole tokens (16 / G per tile), each tile streaming only the pages up to
+    its last token. Ragged counts (a tile may be partly or wholly unused),
+    contexts where early tiles stop inside a full page, at a page edge or in
+    the tail."""
+    _print_case("mq_wide_tiles", group=g, max_q=max_q)
+    ctx = np.array([max_q, max_q + 1, 100, 257, 1000, 2000, 64, 47], dtype=np.int64)
+    hkv = 2
+    wl = W.Workload(f"mq-wide-g{g}", 1, len(ctx), g * hkv, hkv, ("fixed", 1),
+                    ("frac", 0.02, 8.0, 20.0), seed=90 + g)
+    case = LayerCase(wl, ctx_lens=ctx)
+    case.prefill()
+    r = np.random.default_rng(g)
+    t_counts = np.minimum(r.integers(1, max_q + 1, size=len(ctx)), ctx)
+    t_counts[0] = max_q                      # the whole context is new: a first prefill chunk
+    t_counts[1] = max_q
+    t_counts[4] = 1
+    q, cu, out = _run(case, t_counts, max_q, seed=800 + g)
+    _check(case, range(len(ctx)), q, cu, out)
+
+
+def test_mq_prefill_chunks_cover_a_sequence():
+    """Chunked prefill: a 700-token sequence appended and attended in chunks of
+    256, 256 and 188 tokens gives, token for token, the causal attention of the
+    whole sequence (each chunk against everything before it)."""
+    _print_case("mq_prefill_chunks")
+    wl = W.Workload("mq-chunks", 1, 1, 32, 8, ("fixed", 1), ("frac", 0.02, 8.0, 20.0), seed=97)
+    full = LayerCase(wl, ctx_lens=[700])
+    k_all, v_all = full.seq_kv(0)
+    q_all = W.normal_fp16((700, wl.hq, wl.head_dim), 4343, "cuda")
+    pos, outs = 0, []
+    for n in (256, 256, 188):
+        cu_new = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+        slot = torch.tensor([pos], dtype=torch.int32, device="cuda")
+        full.cache.append(k_all[pos:pos + n].contiguous(), v_all[pos:pos + n].contiguous(), cu_new,
+                          slot, n, full.block_table)
+        ctx = torch.tensor([pos + n], dtype=torch.int32, device="cuda")
+        outs.append(full.cache.attend(q_all[pos:pos + n].contiguous(), cu_new, n, full.block_table,
+                                      ctx, pos + n))
+        pos += n
+    torch.cuda.synchronize()
+    got = torch.cat(outs).float().cpu().numpy()
+    kh, vh = oracle.dequantized_sequence(oracle.sequence_cache(k_all.cpu().numpy(),
+                                                               v_all.cpu().numpy()))
+    want = oracle.multiquery_attention(q_all.cpu().numpy(), kh, vh)
+    ok, max_abs, rel = parity.attention_ok(got.reshape(-1, 128), want.reshape(-1, 128))
+    print(f"  chunked prefill max_abs={max_abs:.2e} rel_l2={rel:.2e}", flush=True)
+    assert ok, (max_abs, rel)
+
+
+@pytest.mark.timeout(600)
+def test_mq_wide_full_size_sampled():
+    """The 8B-shaped layer with 128 new tokens per sequence (32 tiles of 4
+    tokens per sequence, 4096 virtual sequences); two sequences checked."""
+    _print_case("mq_wide_full_size_sampled", workload="llama3.1-8b-decode", max_q=128)
+    case = LayerCase(W.WORKLOADS["llama3.1-8b-decode"])
+    case.prefill()
+    t_counts = np.full(case.wl.batch, 128)
+    t_counts[5] = 77
+    q, cu, out = _run(case, t_counts, 128, seed=900)
+    _check(case, [0, 5], q, cu, out)
