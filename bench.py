@@ -201,43 +201,169 @@ def run_decode_bench(wl, steps, warmup, append, fused=True):
     return res
 
 
-def cpu_baseline(wl, budget_s=12.0, n_seqs=32, max_passes=50):
-    """The CPU oracle on a bounded sample of the same workload: decode
-    attention (dequantize the int4 pages, then softmax attention in fp64) of
-    layer 0 for the first `n_seqs` sequences, repeated as decode passes over
-    the unchanged cache until about `budget_s` seconds of timed work. Building
-    the sample's cache with the oracle quantizer happens before the clock
-    starts."""
+def prefill_layer(cache, wl, layer, ctx, plan, bt):
+    """Bulk prefill of one layer's int4 cache through s4kv_quantize_append: a
+    shared prefix (if the workload has one) once into its physical pages, then
+    every sequence's own tokens (after its aliased prefix pages)."""
+    import torch
+    from int4_kivi_quantized_amd import Shape
+    from int4_kivi_quantized_amd.cache import LayerCache
+    mult = W.k_channel_multipliers(wl, layer)
+    alias = np.zeros(wl.batch, dtype=np.int64)
+    if len(plan.sharing):
+        share_pages = wl.shared_prefix // wl.page
+        pk, pv = W.prefix_kv(wl, layer, "cuda", mult)
+        pshape = Shape(1, wl.hq, wl.hkv, plan.num_pages, share_pages)
+        scratch = LayerCache(Shape(1, wl.hq, wl.hkv, 1, share_pages))
+        pbt = torch.from_numpy(plan.prefix_pages[None, :].copy()).cuda()
+        from int4_kivi_quantized_amd import s4kv
+        s4kv.s4kv_quantize_append(pshape, pk.contiguous(), pv.contiguous(),
+                                  torch.tensor([0, wl.shared_prefix], dtype=torch.int32, device="cuda"),
+                                  torch.zeros(1, dtype=torch.int32, device="cuda"), wl.shared_prefix,
+                                  pbt, cache.pages, scratch.tail_k, scratch.tail_v)
+        for b in plan.sharing:
+            alias[b] = min(share_pages, int(ctx[b]) // wl.page)
+    ks, vs, starts, counts = [], [], [], []
+    for b in range(wl.batch):
+        k, v = W.sequence_kv(wl, layer, b, int(ctx[b]), "cuda", mult)
+        st = int(alias[b]) * wl.page
+        ks.append(k[st:])
+        vs.append(v[st:])
+        starts.append(st)
+        counts.append(int(ctx[b]) - st)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device="cuda")
+    sl = torch.tensor(np.asarray(starts, dtype=np.int32), device="cuda")
+    cache.append(torch.cat(ks).contiguous(), torch.cat(vs).contiguous(), cu, sl, max(counts), bt)
+    torch.cuda.synchronize()
+    return alias
+
+
+def small_configs(calls=20, warmup=3):
+    """The configurations checked for correctness, also reported in KV GB/s:
+    the tiny case (one 256-token sequence: latency-bound); the 3B-shaped
+    layer over 8 replicas called in rotation (its 97 MB cache fits in the
+    256 MB last-level cache, so back-to-back calls on one copy would read it
+    from there); the shared-prefix layer over 4 replicas in rotation, with
+    logical bytes (every sequence's pages, shared ones once per reader) and
+    unique bytes (each shared page once). Decode calls (s4kv_paged_decode),
+    each between two HIP events on its stream; medians."""
+    import torch
+    from int4_kivi_quantized_amd import Shape
+    from int4_kivi_quantized_amd.cache import LayerCache
+
+    out = {}
+    for name, reps in (("tiny", 1), ("llama3.2-3b-layer", 8), ("qwen2.5-7b-shared-prefix", 4)):
+        wl = W.WORKLOADS[name]
+        ctx = W.context_lengths(wl)
+        plan = W.plan_pages(wl, ctx)
+        shape = Shape(wl.batch, wl.hq, wl.hkv, plan.num_pages, plan.max_pages)
+        bt = torch.from_numpy(plan.block_table).cuda()
+        ctx_g = torch.from_numpy(ctx.astype(np.int32)).cuda()
+        q = W.queries(wl, 0, "cuda")
+        caches = [LayerCache(shape) for _ in range(reps)]
+        alias = None
+        for c in caches:
+            alias = prefill_layer(c, wl, 0, ctx, plan, bt)
+        o = torch.empty_like(q)
+        max_ctx = int(ctx.max())
+        for _ in range(warmup):
+            for c in caches:
+                c.decode(q, bt, ctx_g, max_ctx, out=o)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls * reps)]
+        torch.cuda.synchronize()
+        for i in range(calls):
+            for r, c in enumerate(caches):
+                a, b = ev[i * reps + r]
+                a.record()
+                c.decode(q, bt, ctx_g, max_ctx, out=o)
+                b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        nb = A.decode_bytes(ctx, wl.hq, wl.hkv)
+        leg = {"batch": wl.batch, "q_heads": wl.hq, "kv_heads": wl.hkv, "replicas": reps,
+               "calls": calls * reps, "call_ms": round(ms, 5), "bytes_per_call": nb,
+               "gbs": round(nb / (ms * 1e-3) / 1e9, 2),
+               "hbm_peak_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "decode_tokens_per_s": round(wl.batch / (ms * 1e-3), 1)}
+        if len(plan.sharing):
+            ub = A.decode_bytes_unique(ctx, wl.hq, wl.hkv, alias)
+            leg["bytes_per_call_logical"] = nb
+            leg["bytes_per_call_unique"] = ub
+            leg["gbs_unique"] = round(ub / (ms * 1e-3) / 1e9, 2)
+        out[name] = leg
+        print(f"[bench] {name}: {ms * 1000:.1f} us per call, {leg['gbs']:.0f} GB/s", file=sys.stderr,
+              flush=True)
+        del caches
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(t_attn=1.5, max_passes=50):
+    """The CPU oracle on bounded samples of the workloads it validates, on the
+    host's cores: the tiny case and the 3B-shaped layer in full, then layer 0
+    of the 8B-shaped workload (its first 16 sequences), of the shared-prefix
+    workload (first 8) and of the 70B-shaped workload (first 2). For each
+    sample the oracle's quantizer (sequence_cache: every page of every
+    sequence, plus the tails) is timed once, and its decode attention
+    (dequantize the pages, then softmax attention in fp64) is repeated until
+    about ``t_attn`` seconds; the two are reported separately, each in GB/s
+    by the same byte accounting as the GPU path (quantize: fp16 K/V read,
+    pages and tails written; attention: the decode bytes). ``value`` is the
+    8B-shaped sample's attention rate. Nothing is extrapolated."""
     import oracle
     import threadpoolctl
 
     info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] + [1])
-    ctx = W.context_lengths(wl)[:n_seqs]
-    mult = W.k_channel_multipliers(wl, 0)
-    q = W.queries(wl, 0, "cpu").numpy()
-    caches = []
-    for b in range(len(ctx)):
-        k, v = W.sequence_kv(wl, 0, b, int(ctx[b]), "cpu", mult)
-        caches.append(oracle.sequence_cache(k.numpy(), v.numpy()))
-    pass_bytes = A.decode_bytes(ctx, wl.hq, wl.hkv)
-    passes, elapsed = 0, 0.0
-    while elapsed < budget_s and passes < max_passes:
+    blas_threads = max([i.get("num_threads", 1) for i in info] + [1])
+    legs = {}
+    for name, n_seqs in (("tiny", None), ("llama3.2-3b-layer", None), ("llama3.1-8b-decode", 16),
+                         ("qwen2.5-7b-shared-prefix", 8), ("llama3-70b", 2)):
+        wl = W.WORKLOADS[name]
+        ctx = W.context_lengths(wl)[:n_seqs]
+        mult = W.k_channel_multipliers(wl, 0)
+        q = W.queries(wl, 0, "cpu").numpy()
+        kvs = []
+        for b in range(len(ctx)):
+            k, v = W.sequence_kv(wl, 0, b, int(ctx[b]), "cpu", mult)
+            kvs.append((k.numpy(), v.numpy()))
         t = time.perf_counter()
-        for b, c in enumerate(caches):
-            kh, vh = oracle.dequantized_sequence(c)
-            oracle.decode_attention(q[b], kh, vh)
-        elapsed += time.perf_counter() - t
-        passes += 1
+        caches = [oracle.sequence_cache(k, v) for k, v in kvs]
+        t_q = time.perf_counter() - t
+        del kvs
+        full = (ctx // 16) * 16
+        q_bytes = A.quantize_bytes(int(full.sum()), int((ctx - full).sum()), wl.hkv)
+        d_bytes = A.decode_bytes(ctx, wl.hq, wl.hkv)
+        passes, t_a = 0, 0.0
+        while (t_a < t_attn or passes == 0) and passes < max_passes:
+            t = time.perf_counter()
+            for b, c in enumerate(caches):
+                kh, vh = oracle.dequantized_sequence(c)
+                oracle.decode_attention(q[b], kh, vh)
+            t_a += time.perf_counter() - t
+            passes += 1
+        legs[name] = {
+            "layer": 0, "sequences": int(len(ctx)), "ctx_sum": int(ctx.sum()),
+            "quantize_s": round(t_q, 3), "quantize_gbs": round(q_bytes / t_q / 1e9, 4),
+            "attention_passes": passes, "attention_s": round(t_a, 3),
+            "attention_gbs": round(d_bytes * passes / t_a / 1e9, 4),
+            "decode_tokens_per_s": round(len(ctx) * passes / t_a, 3),
+        }
+        print(f"[bench] cpu oracle {name}: quantize {legs[name]['quantize_gbs']} GB/s, "
+              f"attention {legs[name]['attention_gbs']} GB/s", file=sys.stderr, flush=True)
+    head = legs["llama3.1-8b-decode"]
     return {
-        "value": round(pass_bytes * passes / elapsed / 1e9, 4),
+        "value": head["attention_gbs"],
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"{wl.name} layer 0, sequences 0..{len(ctx) - 1} (ctx sum {int(ctx.sum())}), "
-                  f"{passes} decode passes over the same cache, {elapsed:.1f} s of CPU time; "
-                  f"host cores visible {len(os.sched_getaffinity(0))}",
-        "tokens_per_s_one_layer": round(len(ctx) * passes / elapsed, 3),
+        "sample": ("numpy oracle on the host: decode attention (dequantize + fp64 softmax "
+                   "attention) of layer 0, first 16 sequences of llama3.1-8b-decode, repeated "
+                   f"{head['attention_passes']} times ({head['attention_s']} s); quantizer and "
+                   "the other configurations' samples under 'legs'"),
+        "host_cores": len(os.sched_getaffinity(0)),
+        "blas_threads": int(blas_threads),
+        "legs": legs,
     }
 
 
@@ -569,9 +695,14 @@ def main():
         print("[bench] multi-query (verify) attention", file=sys.stderr, flush=True)
         line["multiquery"] = multiquery_leg(wl)
         torch.cuda.empty_cache()
+    if not args.no_secondary:
+        print("[bench] small configurations (tiny, 3B rotated, shared prefix)", file=sys.stderr,
+              flush=True)
+        line["small_configs"] = small_configs()
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl)
+        line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line))
 
 

@@ -104,3 +104,25 @@ def test_append_step_bytes():
     ctx = [1, 16, 17, 0]
     want = 2 * (3 * 512 + 2 * 512 + (15 * 512 + 2624))
     assert A.append_step_bytes(ctx, 2) == want == 25728
+
+
+def test_unique_bytes_count_each_shared_chunk_once():
+    """Brute force: enumerate the (physical page, KV head) chunks every sequence
+    reads and count distinct ones."""
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        b, hkv, share = int(rng.integers(2, 9)), int(rng.integers(1, 5)), int(rng.integers(1, 6))
+        ctx = rng.integers(1, 200, size=b)
+        sharing = rng.random(b) < 0.5
+        alias = np.where(sharing, np.minimum(share, ctx // 16), 0)
+        chunks, next_id = set(), 1000
+        logical_full = 0
+        for i in range(b):
+            for p in range(int(ctx[i]) // 16):
+                pid = p if p < alias[i] else (next_id := next_id + 1)
+                for h in range(hkv):
+                    chunks.add((pid, h))
+                logical_full += hkv
+        logical = A.decode_bytes(ctx, 4 * hkv, hkv)
+        unique = A.decode_bytes_unique(ctx, 4 * hkv, hkv, alias)
+        assert logical - unique == (logical_full - len(chunks)) * A.CHUNK_BYTES

@@ -114,3 +114,18 @@ def quantize_bytes(n_tokens_flushed_pages, n_tail_tokens, kv_heads):
     pages = n_tokens_flushed_pages // PAGE
     return int(kv_heads * (n_tokens_flushed_pages * FP16_TOKEN_BYTES + pages * CHUNK_BYTES
                            + 2 * n_tail_tokens * FP16_TOKEN_BYTES))
+
+
+def decode_bytes_unique(ctx_lens, num_q_heads, kv_heads, alias_pages, chunk_bytes=CHUNK_BYTES):
+    """decode_bytes with every shared page counted once.
+
+    ``alias_pages[b]``: how many of sequence b's first pages are shared pages
+    (the sequences that share a prefix all alias its first pages, so the
+    shared pages read by anyone are the first max(alias_pages) of them).
+    decode_bytes counts a shared page once per sequence that reads it (logical
+    bytes, what attention consumes); this counts each physical shared page
+    once (unique bytes, what HBM must deliver when repeated reads of a page
+    hit in a cache). Block-table entries stay counted per reader."""
+    a = np.asarray(alias_pages, dtype=np.int64)
+    dup = int(a.sum() - (a.max() if a.size else 0))
+    return decode_bytes(ctx_lens, num_q_heads, kv_heads, chunk_bytes) - kv_heads * chunk_bytes * dup
