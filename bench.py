@@ -7,7 +7,9 @@ default each layer's step is one s4kv_paged_decode_append call (append and
 decode in one launch of the decode stream, then the split merge);
 --separate-append times s4kv_quantize_append followed by s4kv_paged_decode
 instead. Inputs (caches, queries, new tokens, context lengths) are resident
-in HBM before the timed region.
+in HBM before the timed region. Each timed step (all layers' calls) is
+captured in a HIP graph beforehand and replayed; the same steps launched
+eagerly from Python are timed beside it (--eager times those alone).
 
 Headline workload: Llama-3.1-8B-shaped decode, 32 layers, 32 query / 8 KV
 heads, head_dim 128, batch 128, contexts U[2048, 8192], page 16.
@@ -110,12 +112,15 @@ class Model:
         torch.cuda.synchronize()
 
 
-def run_decode_bench(wl, steps, warmup, append, fused=True):
+def run_decode_bench(wl, steps, warmup, append, fused=True, graph=True):
     import torch
 
-    # warm-up steps, the timed steps (no per-call events inside), then as many
-    # steps again with HIP events around every call for the per-call figures
-    total = warmup + 2 * steps
+    # warm-up steps; `steps` steps timed as eager launches; with `graph`, as
+    # many steps again, each captured in a HIP graph beforehand and timed as
+    # graph replays (the headline); then as many steps with HIP events around
+    # every call for the per-call figures. Every step appends at its own
+    # position, so each timed step does a step's full work.
+    total = warmup + (3 if graph else 2) * steps
     model = Model(wl, total if append else 0, time_prefill=not append)
     B = wl.batch
     max_ctx = int(model.ctx0.max()) + (total if append else 0)
@@ -156,6 +161,16 @@ def run_decode_bench(wl, steps, warmup, append, fused=True):
     for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
+    graphs = []
+    if graph:
+        # one graph per step (the steps' context lengths differ); capturing
+        # launches nothing
+        for i in range(steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(warmup + steps + i)
+            graphs.append(g)
+        torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -165,10 +180,26 @@ def run_decode_bench(wl, steps, warmup, append, fused=True):
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    step_ms = t0.elapsed_time(t1) / steps
+    eager_ms = t0.elapsed_time(t1) / steps
+    step_ms = eager_ms
+    timed0 = warmup
+    if graph:
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        g0.record()
+        for g in graphs:
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        step_ms = g0.elapsed_time(g1) / steps
+        timed0 = warmup + steps
+    del graphs
     # per-call durations: the next `steps` steps, each call between two events
+    ev0 = total - steps
     for i in range(steps):
-        step(warmup + steps + i, i)
+        step(ev0 + i, i)
     torch.cuda.synchronize()
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
 
@@ -180,12 +211,14 @@ def run_decode_bench(wl, steps, warmup, append, fused=True):
         if append and fused:
             nb += A.append_step_bytes(ctx_s, wl.hkv)
         return nb
-    per_layer = [layer_bytes(warmup + i) for i in range(steps)]            # timed steps
-    per_call = [layer_bytes(warmup + steps + i) for i in range(steps)]     # per-call steps
+    per_layer = [layer_bytes(timed0 + i) for i in range(steps)]            # timed steps
+    per_call = [layer_bytes(ev0 + i) for i in range(steps)]                # per-call steps
     step_bytes = float(np.mean(per_layer)) * wl.layers
     dec_bytes = float(np.mean(per_call))
     res = {
         "step_ms": step_ms,
+        "eager_step_ms": eager_ms,
+        "graph": graph,
         "step_bytes": step_bytes,
         "wall_s": wall,
         "kv_gbs": step_bytes / (step_ms * 1e-3) / 1e9,
@@ -564,6 +597,63 @@ def multiquery_leg(wl, max_q=4, calls=20, warmup=3):
     }
 
 
+def prefill_chunk_leg(wl, t_new=128, calls=10, warmup=2):
+    """Chunked-prefill attention: t_new new tokens per sequence (already
+    appended, the last t_new positions of each context) attend causally over
+    layer 0 of the workload's int4 cache in one s4kv_paged_attention_mq call;
+    with Hq/Hkv = 4 the tokens go to the matrix cores in column tiles of 4
+    tokens. Reported: query tokens per second, and the attention's
+    arithmetic rate: for each query token and query head, 2 * 128 flops for
+    the logit and 2 * 128 for the output per visible cache position, against
+    the fp16 dense matrix-core peak. HIP-event medians."""
+    import torch
+    from int4_kivi_quantized_amd import Shape
+    from int4_kivi_quantized_amd.cache import LayerCache
+
+    ctx = W.context_lengths(wl)
+    plan = W.plan_pages(wl, ctx)
+    shape = Shape(wl.batch, wl.hq, wl.hkv, plan.num_pages, plan.max_pages)
+    bt = torch.from_numpy(plan.block_table).cuda()
+    cache = LayerCache(shape)
+    prefill_layer(cache, wl, 0, ctx, plan, bt)
+    ctx_g = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    t_counts = np.full(wl.batch, t_new)
+    qm = W.normal_fp16((int(t_counts.sum()), wl.hq, wl.head_dim), 4545, "cuda")
+    cu_q = torch.from_numpy(np.concatenate([[0], np.cumsum(t_counts)]).astype(np.int32)).cuda()
+    out = torch.empty_like(qm)
+    max_ctx = int(ctx.max())
+    for _ in range(warmup):
+        cache.attend(qm, cu_q, t_new, bt, ctx_g, max_ctx, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        cache.attend(qm, cu_q, t_new, bt, ctx_g, max_ctx, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del cache, qm, out
+    torch.cuda.empty_cache()
+    # visible positions of token t (0-based among the new ones): ctx - t_new + t + 1
+    visible = int(sum(t_new * (c - t_new) + t_new * (t_new + 1) // 2 for c in ctx))
+    flops = 4.0 * wl.head_dim * wl.hq * visible
+    tflops = flops / (ms * 1e-3) / 1e12
+    gq = wl.hq // wl.hkv
+    tile = max(1, 16 // gq)
+    return {
+        "workload": f"{wl.name}, layer 0, {t_new} new tokens per sequence (causal)",
+        "calls": calls,
+        "call_ms": round(ms, 4),
+        "query_tokens_per_s": round(int(t_counts.sum()) / (ms * 1e-3), 1),
+        "tokens_per_tile": tile,
+        "tiles_per_sequence": -(-t_new // tile),
+        "attention_tflops": round(tflops, 2),
+        "mfma_fp16_peak_tflops": 2500.0,
+        "mfma_peak_frac": round(tflops / 2500.0, 4),
+    }
+
+
 def load_traffic(digest):
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if not os.path.exists(path):
@@ -583,6 +673,9 @@ def main():
     ap.add_argument("--workload", default="llama3.1-8b-decode", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (by default each step is captured in a HIP "
+                         "graph and the headline times graph replays; eager is reported beside it)")
     ap.add_argument("--separate-append", action="store_true",
                     help="time s4kv_quantize_append + s4kv_paged_decode per layer instead of the "
                          "fused s4kv_paged_decode_append")
@@ -613,7 +706,8 @@ def main():
     print(f"[bench] read ceiling {rceil['gbs']:.0f} GB/s (non-temporal), "
           f"{rceil['default_policy']['gbs']:.0f} GB/s (default policy)", file=sys.stderr, flush=True)
     fused = wl.append and not args.separate_append
-    r = run_decode_bench(wl, args.steps, args.warmup, append=wl.append, fused=fused)
+    r = run_decode_bench(wl, args.steps, args.warmup, append=wl.append, fused=fused,
+                         graph=not args.eager)
     del r["model"]
     torch.cuda.empty_cache()
     print(f"[bench] step {r['step_ms']:.3f} ms, {r['kv_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
@@ -648,7 +742,10 @@ def main():
                            "s4kv_quantize_append + s4kv_paged_decode" if wl.append else
                            "s4kv_paged_decode"),
             "profiling_layer_override": args.layers,
+            "launch": ("each step (all layers) captured in a HIP graph, timed as replays"
+                       if r["graph"] else "eager launches"),
         },
+        "eager_ms_per_step": round(r["eager_step_ms"], 4),
         "hbm_peak_frac": round(r["kv_gbs"] / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(r["tokens_per_s"], 1),
         "roofline": {
@@ -656,7 +753,7 @@ def main():
             "kernel": ("one s4kv_paged_decode_append call on one layer (its two launches: decode "
                        "stream with the one-token append, split merge); the timed steps hold "
                        "nothing else, so its average duration is the HIP-event time of the timed "
-                       "region over the calls in it" if fused else
+                       "region (graph replays of whole steps) over the calls in it" if fused else
                        "one s4kv_paged_decode call on one layer (its two launches: decode stream, "
                        "split merge), timed with HIP events around each call on its stream"),
             "achieved": round(call_gbs, 2),
@@ -676,12 +773,13 @@ def main():
     if not args.no_secondary and wl.name != "llama3-70b":
         wl2 = W.WORKLOADS["llama3-70b"]
         print(f"[bench] secondary {wl2.name}", file=sys.stderr, flush=True)
-        r2 = run_decode_bench(wl2, max(3, args.steps // 4), 1, append=False)
+        r2 = run_decode_bench(wl2, max(3, args.steps // 4), 1, append=False, graph=not args.eager)
         del r2["model"]
         torch.cuda.empty_cache()
         line["secondary"] = {
             "workload": wl2.name, "layers": wl2.layers, "batch": wl2.batch,
             "ms_per_step": round(r2["step_ms"], 4), "kv_gbs": round(r2["kv_gbs"], 2),
+            "eager_ms_per_step": round(r2["eager_step_ms"], 4),
             "hbm_peak_frac": round(r2["kv_gbs"] / HBM_PEAK_GBS, 4),
             "decode_tokens_per_s": round(r2["tokens_per_s"], 1),
             "decode_launch_gbs": round(r2["decode_launch_gbs"], 2),
@@ -694,6 +792,9 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] multi-query (verify) attention", file=sys.stderr, flush=True)
         line["multiquery"] = multiquery_leg(wl)
+        torch.cuda.empty_cache()
+        print("[bench] chunked prefill attention", file=sys.stderr, flush=True)
+        line["prefill_chunk"] = prefill_chunk_leg(wl)
         torch.cuda.empty_cache()
     if not args.no_secondary:
         print("[bench] small configurations (tiny, 3B rotated, shared prefix)", file=sys.stderr,

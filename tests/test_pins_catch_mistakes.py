@@ -83,6 +83,17 @@ def _mutants():
             out["pages"][key] = a[..., ::-1, :].copy()     # tokens of a page reversed
         return out
 
+    def codes_from_fp32_scale(x16, axis=-1, bits=4):
+        # codes divided by the fp32 range / qmax instead of the stored fp16 scale
+        qmax = oquant.qmax_of(bits)
+        c, s16, z16 = orig_q(x16, axis, bits)
+        xg = np.moveaxis(np.asarray(x16), axis, -1)
+        s32 = (xg.max(-1).astype(np.float32) - xg.min(-1).astype(np.float32)) / np.float32(qmax)
+        den = np.where(s32 == 0, np.float32(1), s32).astype(np.float32)
+        t = (xg.astype(np.float32) - z16.astype(np.float32)[..., None]) / den[..., None]
+        q = np.where((s16 == 0)[..., None], 0, np.clip(np.rint(t), 0, qmax))
+        return np.moveaxis(q.astype(np.uint8), -1, axis), s16, z16
+
     def attn_wrong_group(q16, khat, vhat, sm_scale=None):
         # query head j reads KV head j % Hkv instead of j // G
         hq, hkv = q16.shape[0], khat.shape[1]
@@ -99,6 +110,7 @@ def _mutants():
         "k_grouped_per_token": ("quantize_groups", oquant,
                                 lambda x, axis=-1, bits=4: _swap(orig_q, x, axis, bits)),
         "keep_negative_zero": ("quantize_groups", oquant, keep_neg_zero),
+        "codes_from_fp32_scale": ("quantize_groups", oquant, codes_from_fp32_scale),
         "dequant_drops_zero": ("dequantize", oquant, drop_zero_point),
         "tail_off_by_one": ("sequence_cache", ocache, tail_off_by_one),
         "page_tokens_reversed": ("sequence_cache", ocache, transposed_pages),
