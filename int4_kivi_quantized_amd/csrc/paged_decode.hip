@@ -689,12 +689,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     start.h = local / start.nunits;
     start.unit = local % start.nunits;
   }
-  // Entry at a cursor: a pair (or single) of pages, or the tail.
-  // Returns the number of units it covers (0 = tail).
-  auto entry_pages = [&](const Cursor& cu) -> int {
-    if (cu.unit >= cu.full) return 0;
-    return (cu.unit + 1 < cu.full && cu.u + 1 < u1) ? 2 : 1;
-  };
   auto advance = [&](Cursor& cu, int n_units) {
     cu.u += n_units;
     cu.unit += n_units;
@@ -737,29 +731,48 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   // their use so the scalar-load latency overlaps a whole iteration. A single
   // page is fetched twice (as pages A and B) so the stage never holds stale
   // scales.
-  auto next_pair = [&](Cursor& cu) -> bool {
-    while (cu.u < u1 && entry_pages(cu) == 0) advance(cu, 1);
-    return cu.u < u1;
-  };
+  // Producer state kept per segment, so that a pair inside a segment costs a
+  // compare, two id loads and the chunk addresses: the end of the segment's
+  // full pages within the range, the segment's block-table row and the base
+  // of its KV head's chunks.
+  bool p_live = false;
+  int p_page_end = 0;
+  const int32_t* p_row = block_table;
+  const uint8_t* p_base = pages;
+  // chunk (id, h) is at pages + (id * Hkv + h) * stride; id * Hkv + h <
+  // num_pages * Hkv fits in 32 bits
+  const uint32_t id_stride = static_cast<uint32_t>(hkv) * PF::kStride;
   int nid_a = 0, nid_b = 0;
-  auto prefetch_ids = [&]() {
-    if (!next_pair(prod)) return;
-    // B * max_pages fits in int32 (the host checks B * Hkv * (max_pages + 1))
+  auto p_ids = [&]() {
     // Both ids load unconditionally (the second index clamped to the row) and
     // the pair / single choice is made where they are used, one pair later,
     // so nothing waits for these scalar loads here.
-    const int32_t* row = block_table + real_seq(prod.b) * max_pages;
-    nid_a = row[prod.unit];
-    nid_b = row[min(prod.unit + 1, max_pages - 1)];
+    nid_a = p_row[prod.unit];
+    nid_b = p_row[min(prod.unit + 1, max_pages - 1)];
+  };
+  // from the cursor (a unit of the range, possibly a tail or the end of a
+  // segment), on to the next full page in the range
+  auto p_seek = [&]() {
+    if (prod.u < u1 && prod.unit >= prod.nunits) advance(prod, 0);
+    while (prod.u < u1 && prod.unit >= prod.full) advance(prod, 1);
+    p_live = prod.u < u1;
+    if (!p_live) return;
+    p_page_end = min(prod.full, prod.unit + (u1 - prod.u));
+    // B * max_pages fits in int32 (the host checks B * Hkv * (max_pages + 1))
+    p_row = block_table + real_seq(prod.b) * max_pages;
+    p_base = pages + static_cast<uint64_t>(static_cast<uint32_t>(prod.h)) * PF::kStride;
+    p_ids();
   };
   // Issue the pair at the producer cursor (tails need no DMA).
   auto produce = [&]() {
-    if (prod.u >= u1) return;
-    const int np = entry_pages(prod);
-    const int idA = nid_a, idB = (np == 2) ? nid_b : nid_a;
-    // chunk index id * Hkv + h < num_pages * Hkv fits in 32 bits
-    const uint8_t* chA = pages + static_cast<uint64_t>(static_cast<uint32_t>(idA * hkv + prod.h)) * PF::kStride;
-    const uint8_t* chB = pages + static_cast<uint64_t>(static_cast<uint32_t>(idB * hkv + prod.h)) * PF::kStride;
+    if (!p_live) return;
+    const int np = (prod.unit + 1 < p_page_end) ? 2 : 1;
+    // the ids are wave-uniform (scalar loads at a uniform address); saying
+    // so keeps the chunk bases in scalar registers, as the DMA form needs
+    const int idA = __builtin_amdgcn_readfirstlane(nid_a);
+    const int idB = __builtin_amdgcn_readfirstlane((np == 2) ? nid_b : nid_a);
+    const uint8_t* chA = p_base + static_cast<uint64_t>(static_cast<uint32_t>(idA)) * id_stride;
+    const uint8_t* chB = p_base + static_cast<uint64_t>(static_cast<uint32_t>(idB)) * id_stride;
     uint8_t* st = stage_s[pstage];
     if (++pstage == kStages) pstage = 0;
     const uint32_t lo = 16u * static_cast<uint32_t>(lane);
@@ -808,8 +821,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
       }
     }
     ++issued;
-    advance(prod, np);
-    prefetch_ids();
+    prod.u += np;
+    prod.unit += np;
+    if (prod.unit < p_page_end) p_ids();
+    else p_seek();
   };
 
   // ---- per-(b, h) state, per column ----
@@ -1261,26 +1276,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     compiler_fence();
     ++consumed;
   };
-  prefetch_ids();
+  p_seek();
 #pragma unroll
   for (int s = 0; s < kStages; ++s) produce();
   Cursor cons = start;
   while (cons.u < u1) {
     begin_segment(cons);
-    // the segment's pages, then its tail if the range reaches it
-    int np = entry_pages(cons);
-    while (np > 0) {
+    // the segment's units in the range: its pages as pairs (a single page
+    // last when their count is odd), then its tail if the range reaches it
+    const int unit_end = min(cons.nunits, cons.unit + (u1 - cons.u));
+    const int page_end = min(unit_end, cons.full);
+    int unit = cons.unit;
+    while (unit < page_end) {
+      const int np = (unit + 1 < page_end) ? 2 : 1;
       // kAppend: with no tail, the segment's last page holds the new token
-      const int fresh_p = (kAppend && cons.tail == 0 && cons.unit + np == cons.full) ? cons.full - 1 : -1;
-      consume_pair(np, cons.unit * kPage, fresh_p);
-      advance(cons, np);
-      np = (cons.u < u1 && cons.b == cur_b && cons.h == cur_h) ? entry_pages(cons) : -1;
+      const int fresh_p = (kAppend && cons.tail == 0 && unit + np == cons.full) ? cons.full - 1 : -1;
+      consume_pair(np, unit * kPage, fresh_p);
+      unit += np;
     }
-    if (np == 0) {
-      process_tail(cons.tail, cons.full * kPage);
-      advance(cons, 1);
-    }
+    if (unit_end > cons.full) process_tail(cons.tail, cons.full * kPage);
     end_segment();
+    advance(cons, unit_end - cons.unit);
   }
   if constexpr (kPacked) store_kept();
 }
