@@ -712,6 +712,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   int pstage = 0, cstage = 0;  // ring slots of the next issue / the next consume
   // kMQ: the column's causal limit (cache position) in the current segment
   int col_lim = 0;
+  // kMQ: the smallest limit among the wave's columns (its tile's first
+  // token), wave-uniform: a pair whose positions all lie at or below it
+  // needs no mask
+  int lim_min = 0;
   auto q_row = [&](int bv, int h) {
     if constexpr (kMQ) {
       // a sequence with fewer new tokens than columns repeats its last token
@@ -721,6 +725,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
       const int q0 = cu_q[b], tb = cu_q[b + 1] - q0;
       const int t = min((bv - b * ct_n) * tpt + head / gq, max(tb - 1, 0));
       col_lim = ctx - tb + t;
+      lim_min = ctx - tb + min((bv - b * ct_n) * tpt, max(tb - 1, 0));
       const int64_t row = min(max((int64_t)q0 + t, (int64_t)0), (int64_t)total_q - 1);
       return reinterpret_cast<const uint8_t*>(q + (row * hq + h * gq + head % gq) * kHeadDim);
     } else {
@@ -1115,9 +1120,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
 #pragma unroll
       for (int k = 0; k < 4; ++k) lg[k] = mine[k] * qk_col + zl;
       if constexpr (kMQ) {
+        if (pos0 + 2 * kPage - 1 > lim_min) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (pos0 + kPage * pslot + 4 * g + k > col_lim) lg[k] = kNegInf;
+          for (int k = 0; k < 4; ++k)
+            if (pos0 + kPage * pslot + 4 * g + k > col_lim) lg[k] = kNegInf;
+        }
       }
       const float mb = rows_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
       rescale_to(mb);
@@ -1190,12 +1197,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
       for (int k = 0; k < 4; ++k) {
         lgA[k] = accA[k] * qk_col + zA * l2s;
         lgB[k] = accB[k] * qk_col + zlB;
-        if constexpr (kMQ) {
-          if (pos0 + 4 * g + k > col_lim) lgA[k] = kNegInf;
-          if (pos0 + kPage + 4 * g + k > col_lim) lgB[k] = kNegInf;
-        }
-        mb = fmaxf(mb, fmaxf(lgA[k], lgB[k]));
       }
+      if constexpr (kMQ) {
+        if (pos0 + 2 * kPage - 1 > lim_min) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (pos0 + 4 * g + k > col_lim) lgA[k] = kNegInf;
+            if (pos0 + kPage + 4 * g + k > col_lim) lgB[k] = kNegInf;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mb = fmaxf(mb, fmaxf(lgA[k], lgB[k]));
       mb = rows_max(mb);
       rescale_to(mb);
       const float msw = m_run;
