@@ -1367,21 +1367,27 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   const int2 ws = seg_waves[bh];
   float M = kNegInf, L = 0.f;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto join = [&](int wv) {
+    const float* sl = slots + ((bh + wv) * G + jj) * kSlotStride;
+    const float ms = sl[kHeadDim], ls = sl[kHeadDim + 1];
+    const f4 os = *reinterpret_cast<const f4*>(sl + d0);
+    if (ms == kNegInf) return;
+    const float Mn = fmaxf(M, ms);
+    const float a = (M == kNegInf) ? 0.f : exp2f(M - Mn);
+    const float c = exp2f(ms - Mn);
+    L = L * a + ls * c;
+    acc = acc * a + os * c;
+    M = Mn;
+  };
   if (live) {
-    for (int wv = ws.x + r; wv <= ws.y; wv += R) {
-      // waves strictly between two owners can have empty ranges (when U < W);
-      // they wrote nothing
-      if ((int64_t)wv * U / W == (int64_t)(wv + 1) * U / W) continue;
-      const float* sl = slots + ((bh + wv) * G + jj) * kSlotStride;
-      const float ms = sl[kHeadDim], ls = sl[kHeadDim + 1];
-      const f4 os = *reinterpret_cast<const f4*>(sl + d0);
-      if (ms == kNegInf) continue;
-      const float Mn = fmaxf(M, ms);
-      const float a = (M == kNegInf) ? 0.f : exp2f(M - Mn);
-      const float c = exp2f(ms - Mn);
-      L = L * a + ls * c;
-      acc = acc * a + os * c;
-      M = Mn;
+    if (U >= W) {
+      // every range holds at least one unit: the waves ws.x .. ws.y
+      for (int wv = ws.x + r; wv <= ws.y; wv += R) join(wv);
+    } else {
+      // every range holds at most one unit, so the (b, h)'s n units sit in
+      // n waves, the owners of its units (the first one's range is that unit)
+      const int64_t first = (int64_t)ws.x * U / W;
+      for (int k = r; k < n; k += R) join(owner_wave(first + k, U, W));
     }
   }
   if (R > 1) {
