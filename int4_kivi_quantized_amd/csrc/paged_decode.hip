@@ -1318,30 +1318,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
 // unit ranges touched (b, h) (recorded by the wave owning its first unit): m in
 // log2 units, O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M the
 // max over the slots s. A block serves hb heads of one (b, h): hb x R slot
-// groups x 32 output quads. Thread group r merges slots r, r + R, ... online
-// (one slot each when R covers them, as the launch sizes it); the groups'
-// maxima meet in LDS, each group rescales to the common maximum, and the R
-// groups add up in a fixed binary tree (same order every call).
+// groups x 32 / QW threads, each thread 4 * QW consecutive outputs. Thread
+// group r merges slots r, r + R, ... online (one slot each when R covers them,
+// as the launch sizes it); the groups' maxima meet in LDS, each group rescales
+// to the common maximum, and the R groups add up in a fixed binary tree (same
+// order every call). QW only changes which thread computes an output, not how:
+// results are the same for every QW.
 // With cu_q (several query tokens per sequence) blockIdx.y is a virtual
 // sequence, column tile bv % ct_n of sequence bv / ct_n (see tile_span), and
 // the G columns of a slot are (token, head) pairs, column jj = token
 // tile * tpt + jj / gq, head jj % gq; columns past the sequence's token count
 // are merged but not stored.
 constexpr int kReduceThreads = 1024;
+template <int QW>
 __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
     const float* __restrict__ slots, const int32_t* __restrict__ total_units,
     const int2* __restrict__ seg_waves, const int32_t* __restrict__ ctx_lens, int32_t max_pages,
     int32_t hkv, int32_t G, int32_t W, __half* __restrict__ out, const int32_t* __restrict__ cu_q,
     int32_t gq, int32_t total_q, int32_t hb, int32_t R, int32_t ct_n, int32_t tpt) {
-  __shared__ float red_m[kReduceThreads / 32], red_l[kReduceThreads / 32];
+  constexpr int kLanes = 32 / QW;  // threads per (head, slot group)
+  // a block has at most kReduceThreads / QW threads (the launch sizes it so)
+  __shared__ float red_m[32], red_l[32];
   __shared__ f4 red_o[kReduceThreads];
   const int groups = (G + hb - 1) / hb;
   const int h = blockIdx.x / groups, b = blockIdx.y;
-  const int t = threadIdx.x;
-  const int q = t & 31, rg = t >> 5;        // output quad; (head, slot group) index
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int q = t % kLanes, rg = t / kLanes;  // output block; (head, slot group) index
   const int r = rg % R, jb = rg / R;
   const int jj = (blockIdx.x % groups) * hb + jb;
-  const int d0 = 4 * q;
+  const int d0 = 4 * QW * q;
   const bool live = jj < G;
   __half* o = nullptr;
   bool store = live;
@@ -1361,22 +1366,27 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   const int64_t bh = (int64_t)b * hkv + h;
   const int64_t U = total_units[0];
   if (n <= 0 || U <= 0) {
-    if (r == 0 && store) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    if (r == 0 && store)
+      for (int i = 0; i < QW; ++i) *reinterpret_cast<uint2*>(o + 4 * i) = make_uint2(0u, 0u);
     return;
   }
   const int2 ws = seg_waves[bh];
   float M = kNegInf, L = 0.f;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  f4 acc[QW];
+  for (int i = 0; i < QW; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
   auto join = [&](int wv) {
     const float* sl = slots + ((bh + wv) * G + jj) * kSlotStride;
     const float ms = sl[kHeadDim], ls = sl[kHeadDim + 1];
-    const f4 os = *reinterpret_cast<const f4*>(sl + d0);
+    f4 os[QW];
+    for (int i = 0; i < QW; ++i) os[i] = *reinterpret_cast<const f4*>(sl + d0 + 4 * i);
     if (ms == kNegInf) return;
     const float Mn = fmaxf(M, ms);
     const float a = (M == kNegInf) ? 0.f : exp2f(M - Mn);
     const float c = exp2f(ms - Mn);
-    L = L * a + ls * c;
-    acc = acc * a + os * c;
+    // one rounding order for every QW: each term is fma(old, a, new * c)
+    L = fmaf(L, a, ls * c);
+    for (int i = 0; i < QW; ++i)
+      for (int k = 0; k < 4; ++k) acc[i][k] = fmaf(acc[i][k], a, os[i][k] * c);
     M = Mn;
   };
   if (live) {
@@ -1396,15 +1406,19 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
     float Mh = kNegInf;
     for (int k = 0; k < R; ++k) Mh = fmaxf(Mh, red_m[jb * R + k]);
     const float a = (M == kNegInf) ? 0.f : exp2f(M - Mh);
-    acc = acc * a;
-    L *= a;
-    red_o[t] = acc;
+    for (int i = 0; i < QW; ++i) {
+      for (int k = 0; k < 4; ++k) acc[i][k] = __fmul_rn(acc[i][k], a);  // not fused into the adds below
+      red_o[i * nt + t] = acc[i];
+    }
+    L = __fmul_rn(L, a);
     if (q == 0) red_l[rg] = L;
     __syncthreads();
     for (int stride = R / 2; stride > 0; stride /= 2) {
       if (r < stride) {
-        acc += red_o[t + 32 * stride];
-        red_o[t] = acc;
+        for (int i = 0; i < QW; ++i) {
+          acc[i] += red_o[i * nt + t + kLanes * stride];
+          red_o[i * nt + t] = acc[i];
+        }
         if (q == 0) {
           L += red_l[rg + stride];
           red_l[rg] = L;
@@ -1416,12 +1430,14 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(
   }
   if (r != 0 || !store) return;
   const float inv = 1.0f / L;
-  __half2 lo = __floats2half2_rn(acc[0] * inv, acc[1] * inv);
-  __half2 hi = __floats2half2_rn(acc[2] * inv, acc[3] * inv);
-  uint2 pk;
-  pk.x = *reinterpret_cast<uint32_t*>(&lo);
-  pk.y = *reinterpret_cast<uint32_t*>(&hi);
-  *reinterpret_cast<uint2*>(o) = pk;
+  for (int i = 0; i < QW; ++i) {
+    __half2 lo = __floats2half2_rn(acc[i][0] * inv, acc[i][1] * inv);
+    __half2 hi = __floats2half2_rn(acc[i][2] * inv, acc[i][3] * inv);
+    uint2 pk;
+    pk.x = *reinterpret_cast<uint32_t*>(&lo);
+    pk.y = *reinterpret_cast<uint32_t*>(&hi);
+    *reinterpret_cast<uint2*>(o + 4 * i) = pk;
+  }
 }
 
 // pages and tails are written only by the kAppend instantiations, whose
@@ -1515,11 +1531,28 @@ hipError_t launch_merge(const s4kv_shape& s, int W, int32_t max_ctx, const Split
   while (R < share && R < 32) R *= 2;
   const int hb = std::max(1, std::min(G, kReduceThreads / (32 * R)));
   const int groups = (G + hb - 1) / hb;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(s.num_kv_heads * groups, s.num_seqs),
-                     dim3(32 * R * hb), 0, stream, ws.slots, ws.total_units,
-                     reinterpret_cast<const int2*>(ws.seg_waves), ctx_lens, s.max_pages_per_seq,
-                     s.num_kv_heads, G, W, static_cast<__half*>(out), cu_q, gq, total_q, hb, R,
-                     ct_n, tpt);
+  // Outputs per thread: 4, or 8 / 16 when four per thread would need more
+  // waves than the GPU holds at once (a merge of many columns or virtual
+  // sequences then runs in one or a few rounds of resident waves, each thread
+  // with several loads in flight, rather than in many rounds of one-load waves).
+  const int64_t threads = (int64_t)s.num_seqs * s.num_kv_heads * groups * 32 * R * hb;
+  const int64_t resident = (int64_t)resident_waves() * 4 * 64;  // 32 waves per CU
+  const int QW = threads <= resident ? 1 : threads <= 2 * resident ? 2 : 4;
+  const dim3 grid(s.num_kv_heads * groups, s.num_seqs), block(32 / QW * R * hb);
+  const int2* segs = reinterpret_cast<const int2*>(ws.seg_waves);
+  __half* o = static_cast<__half*>(out);
+  if (QW == 1)
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, grid, block, 0, stream, ws.slots, ws.total_units,
+                       segs, ctx_lens, s.max_pages_per_seq, s.num_kv_heads, G, W, o, cu_q, gq,
+                       total_q, hb, R, ct_n, tpt);
+  else if (QW == 2)
+    hipLaunchKernelGGL(splitk_reduce_kernel<2>, grid, block, 0, stream, ws.slots, ws.total_units,
+                       segs, ctx_lens, s.max_pages_per_seq, s.num_kv_heads, G, W, o, cu_q, gq,
+                       total_q, hb, R, ct_n, tpt);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<4>, grid, block, 0, stream, ws.slots, ws.total_units,
+                       segs, ctx_lens, s.max_pages_per_seq, s.num_kv_heads, G, W, o, cu_q, gq,
+                       total_q, hb, R, ct_n, tpt);
   return hipGetLastError();
 }
 size_t workspace_for_columns(const s4kv_shape& s, int columns) {
