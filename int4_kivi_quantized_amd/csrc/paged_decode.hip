@@ -114,29 +114,32 @@ __device__ inline void v_operands(uint32_t wa, uint32_t wb, h8& even, h8& odd) {
 }
 
 // 2-bit codes (pages of the 2-bit format): a mask keeps two codes per dword,
-// one in each fp16 half, at bits 0-1 (x 2^-24) or 2-3 (x 2^-22). K operand m
-// from dword m / 2 of the lane's 8 bytes, shifted by 8 for odd m: elements
-// 0,1 / 4,5 carry 2^-24 and 2,3 / 6,7 carry 2^-22, the int4 slot pattern with
-// a ratio of 4 instead of 16.
-constexpr uint32_t kM2Lo = 0x00030003u, kM2Hi = 0x000C000Cu;
+// one in each fp16 half; a code at bits 2j..2j+1 of its half (j = 0..3) is
+// the fp16 subnormal c * 2^(2j - 24). K operand m comes from dword m / 2 of
+// the lane's 8 bytes, shifted by 8 for odd m, and element i sits at j = i / 2:
+// the four element pairs carry 2^-24, 2^-22, 2^-20, 2^-18, and the query
+// side carries 2^-4, 2^-6, 2^-8, 2^-10 on them (every product c q s 2^-28).
+constexpr uint32_t kM2[4] = {0x00030003u, 0x000C000Cu, 0x00300030u, 0x00C000C0u};
 __device__ inline h8 k_operand2(uint32_t w, int odd) {
   const uint32_t x = odd ? (w >> 8) : w;
-  const uint32_t x4 = x >> 4;
   u4 v;
-  v[0] = x & kM2Lo;
-  v[1] = x & kM2Hi;
-  v[2] = x4 & kM2Lo;
-  v[3] = x4 & kM2Hi;
+  v[0] = x & kM2[0];
+  v[1] = x & kM2[1];
+  v[2] = x & kM2[2];
+  v[3] = x & kM2[3];
   return as_h8(v);
 }
 // V tiles 2m and 2m+1 of a pair: tile u lives in dword u / 4 of each page at
-// shift 4 (u % 4); elements 0..3 from page A, 4..7 from page B.
+// shift 4 (u % 4); elements 0..3 from page A, 4..7 from page B. The odd tile
+// is taken in place (j = 2, 3: 2^-20 and 2^-18 where the even tile has 2^-24
+// and 2^-22), so its products carry 2^-20 where the even tile's carry 2^-24
+// (PairFmt::kOddTileUnscale undoes that).
 __device__ inline void v_operands2(uint32_t wa, uint32_t wb, int m, h8& even, h8& odd) {
   const int sh = 8 * (m & 1);
-  const uint32_t ea = wa >> sh, eb = wb >> sh, oa = ea >> 4, ob = eb >> 4;
+  const uint32_t ea = wa >> sh, eb = wb >> sh;
   u4 e, o;
-  e[0] = ea & kM2Lo; e[1] = ea & kM2Hi; e[2] = eb & kM2Lo; e[3] = eb & kM2Hi;
-  o[0] = oa & kM2Lo; o[1] = oa & kM2Hi; o[2] = ob & kM2Lo; o[3] = ob & kM2Hi;
+  e[0] = ea & kM2[0]; e[1] = ea & kM2[1]; e[2] = eb & kM2[0]; e[3] = eb & kM2[1];
+  o[0] = ea & kM2[2]; o[1] = ea & kM2[3]; o[2] = eb & kM2[2]; o[3] = eb & kM2[3];
   even = as_h8(e);
   odd = as_h8(o);
 }
@@ -251,11 +254,14 @@ __device__ inline void zero_terms(const h8 (&qh)[4], const u4 (&z)[4], float& ta
 // kStages (per code width): the wave reads a stage into registers and
 // refills it at once, so the next pairs load while this one is computed.
 
-// Per code width: stage geometry, DMA count, chunk pitch, and the factors of
-// the second slot group (query side, probability side); see k_operand /
-// k_operand2. kLazy bounds p: the largest V scale is (65504 + 65504) / qmax
-// (< 2^13.1 for int4, < 2^15.42 for 2 bits), and p * sV must stay below the
-// fp16 maximum 65504 (2^15.999).
+// Per code width: stage geometry, DMA count, chunk pitch, the query-side
+// factor of each K element pair (q_factor), the probability-side factor of
+// the second slot group, and the unscale of the odd V tiles; see k_operand /
+// k_operand2 / v_operands2. kLazy bounds p (p <= 2^kLazy): the largest V
+// scale is (65504 + 65504) / qmax (< 2^13.1 for int4, < 2^15.42 for 2 bits),
+// and p * sV must stay below the fp16 maximum 65504 (2^15.999). kLead: a
+// column's reference max, when it moves, is set this far above the new
+// maximum, so the next move needs a logit kLazy + kLead above that maximum.
 template <int kBits>
 struct PairFmt;
 //
@@ -274,8 +280,11 @@ struct PairFmt<4> {
   // one stage: deeper rings measured slower (more bytes in flight per wave
   // only queue longer at this rate)
   static constexpr int kStages = 1;
-  static constexpr float kQSlot23 = 0.00390625f, kPSlot23 = 0.0625f;  // 2^-8, 1/16
-  static constexpr float kLazy = 2.0f;
+  static constexpr float kPSlot23 = 0.0625f;  // 1/16
+  // element pairs 0,1 / 4,5: 2^-4; 2,3 / 6,7: 2^-8
+  __device__ static constexpr float q_factor(int j) { return (j & 1) ? 0.00390625f : 0.0625f; }
+  static constexpr float kOddTileUnscale = 16777216.0f;  // 2^24, as the even tiles
+  static constexpr float kLazy = 2.0f, kLead = 0.0f;
 };
 template <>
 struct PairFmt<2> {
@@ -283,8 +292,15 @@ struct PairFmt<2> {
   static constexpr int kQExp = 4;
   static constexpr int kStride = kK2ChunkStride;
   static constexpr int kStages = 1;
-  static constexpr float kQSlot23 = 0.015625f, kPSlot23 = 0.25f;  // 2^-6, 1/4
-  static constexpr float kLazy = 0.5f;
+  static constexpr float kPSlot23 = 0.25f;  // 1/4
+  // element pair j: 2^-(4 + 2j)
+  __device__ static constexpr float q_factor(int j) {
+    return j == 0 ? 0.0625f : j == 1 ? 0.015625f : j == 2 ? 0.00390625f : 0.0009765625f;
+  }
+  static constexpr float kOddTileUnscale = 1048576.0f;  // 2^20
+  // p <= 1 (p * sV < 2^15.42); with the lead the reference max moves as
+  // rarely as with int4's bound of 4
+  static constexpr float kLazy = 0.0f, kLead = 2.0f;
 };
 
 // Every cache byte is read once: the loads carry the non-temporal policy (nt),
@@ -838,6 +854,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   float m_run = kMEmpty, l_part = 0.f, lz_part = 0.f;
   f4 o[8];
   int cur_b = -1, cur_h = 0;
+  // unscale of the page products accumulated in output tile t
+  auto tile_unscale = [](int t) { return (t & 1) ? PF::kOddTileUnscale : kPvUnscale; };
 
   auto begin_segment = [&](const Cursor& cu) {
     const int b = cu.b, h = cu.h;
@@ -870,11 +888,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // element i of product m is channel 32m+8g+i, pre-scaled by 2^E times
-      // 2^-4 (slots 0,1,4,5) or the second slot group's factor (slots 2,3,6,7)
+      // the factor of its element pair i / 2
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        qc[m][i] = static_cast<_Float16>(static_cast<float>(qh[m][i]) * pre *
-                                         (((i & 2) == 0) ? 0.0625f : PF::kQSlot23));
+        qc[m][i] = static_cast<_Float16>(static_cast<float>(qh[m][i]) * pre * PF::q_factor(i >> 1));
     }
     m_run = kMEmpty;
     l_part = 0.f;
@@ -892,6 +909,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   // kCopies columns, so each copy keeps a different 1/kCopies of the outputs.
   constexpr int kCopies = kHiLoCols ? 4 : 2;  // columns holding the same head
   constexpr int kKeep = 8 / kCopies;          // output tiles kept per lane
+  // kept tile n is output tile kKeep * copy + n, of the parity of n
+  static_assert(kKeep % 2 == 0, "kept tiles keep their parity");
   const int copy = kHiLoCols ? (c >> 2) : (c >> 3);
   const int head_col = kHiLoCols ? (c & 3) : (c & 7);
   f4 keep_o[kKeep];
@@ -949,7 +968,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
         for (int k = 1; k < kCopies; ++k)
           if (copy == k) v = ov[kKeep * k + n];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) keep_o[n][i] = v[i] * kPvUnscale + lz;
+        for (int i = 0; i < 4; ++i) keep_o[n][i] = v[i] * tile_unscale(n) + lz;
       }
       keep_m = m_out;
       keep_l = l;
@@ -961,7 +980,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
         for (int t = 0; t < 8; ++t) {
           f4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = ov[t][i] * kPvUnscale + lz;
+          for (int i = 0; i < 4; ++i) v[i] = ov[t][i] * tile_unscale(t) + lz;
           *reinterpret_cast<f4*>(dst + 16 * t + 4 * g) = v;
         }
         if (g == 0) { dst[kHeadDim] = m_out; dst[kHeadDim + 1] = l; }
@@ -976,7 +995,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
   auto rescale_to = [&](float mb) {
     const bool up = mb > m_run + PF::kLazy;
     if (__any(up)) {
-      const float mnew = up ? mb : m_run;
+      const float mnew = up ? (PF::kLead != 0.f ? mb + PF::kLead : mb) : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
       l_part *= alpha;
       lz_part *= alpha;
@@ -1065,8 +1084,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
         ot = mfma(a, bhi, ot);
         ot = mfma(a, blo, ot);
       }
-      // the pages' products carry 2^-24; bring the tail's to that scale (exact)
-      o[t] += ot * (1.0f / kPvUnscale);
+      // bring the tail's products to the pages' scale for tile t (exact)
+      o[t] += ot * (1.0f / tile_unscale(t));
     }
     __builtin_amdgcn_wave_barrier();
   };
