@@ -303,9 +303,11 @@ struct PairFmt<2> {
   static constexpr float kLazy = 0.0f, kLead = 2.0f;
 };
 
-// Every cache byte is read once: the loads carry the non-temporal policy (nt),
-// which streams them past the caches; on MI355X a pure read of 4 KB chunks
-// runs at about 6.8-7.0 TB/s this way against about 6.0 TB/s without it.
+// A decode call reads every cache byte once: its loads carry the non-temporal
+// policy (nt), which streams them past the caches; on MI355X a pure read of
+// 4 KB chunks runs at about 6.8-7.0 TB/s this way against about 6.0 TB/s
+// without it. (Column tiles of one sequence read the same pages at about the
+// same time, and keep the default policy, so that the caches serve repeats.)
 // 16 bytes per lane from base + off (base wave-uniform, held in SGPRs; off the
 // lane's 32-bit offset) to LDS at lds_base + 16 * lane, non-temporal. The
 // SGPR-base address form costs no 64-bit vector address arithmetic per load
@@ -313,15 +315,25 @@ struct PairFmt<2> {
 // 64-bit VGPR address for every load). The compiler sets M0 (the LDS base)
 // for the operand; the s_nop is the wait state between that write and the
 // load that reads it.
+template <bool kNT = true>
 __device__ inline void dma16_at(const uint8_t* base, uint32_t off, uint8_t* lds_base) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) uint8_t*)(lds_base)));
-  __asm__ __volatile__(
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1 nt"
-      :
-      : "v"(off), "s"(base), "{m0}"(m0)
-      : "memory");
+  if constexpr (kNT) {
+    __asm__ __volatile__(
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(off), "s"(base), "{m0}"(m0)
+        : "memory");
+  } else {
+    __asm__ __volatile__(
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(off), "s"(base), "{m0}"(m0)
+        : "memory");
+  }
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -798,14 +810,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ?
     if (++pstage == kStages) pstage = 0;
     const uint32_t lo = 16u * static_cast<uint32_t>(lane);
     if constexpr (kBits == 4) {
-      dma16_at(chA, lo + kOffKCodes, st + 0);
-      dma16_at(chB, lo + kOffKCodes, st + 1024);
-      dma16_at(chA, lo + kOffVCodes, st + 2048);
-      dma16_at(chB, lo + kOffVCodes, st + 3072);
-      if (lane < 36) {
-        dma16_at(chA, lo + kOffKScale, st + 4096);
-        dma16_at(chB, lo + kOffKScale, st + 4672);
-      }
+      auto issue = [&](auto nt) {
+        constexpr bool kNT = decltype(nt)::value;
+        dma16_at<kNT>(chA, lo + kOffKCodes, st + 0);
+        dma16_at<kNT>(chB, lo + kOffKCodes, st + 1024);
+        dma16_at<kNT>(chA, lo + kOffVCodes, st + 2048);
+        dma16_at<kNT>(chB, lo + kOffVCodes, st + 3072);
+        if (lane < 36) {
+          dma16_at<kNT>(chA, lo + kOffKScale, st + 4096);
+          dma16_at<kNT>(chB, lo + kOffKScale, st + 4672);
+        }
+      };
+      // several column tiles per sequence: the default policy (see dma16_at)
+      if (kMQ && ct_n > 1)
+        issue(std::false_type{});
+      else
+        issue(std::true_type{});
     } else {
       dma16_at(chA, lo, st + 0);
       dma16_at(chB, lo, st + 1024);
