@@ -590,9 +590,16 @@ constexpr int kSlotStride = kHeadDim + 4;  // 128 outputs, m, l, 2 pad (16-byte 
 // page (15 tail tokens and the new one) into the pool and into its ring stage.
 // Either way it attends over the new token straight from its inputs.
 // Waves per SIMD: two, or three with 2-bit codes, whose pairs carry fewer
-// bytes for the same instruction count (the 2-bit kernel fits 168 VGPRs).
+// bytes for the same instruction count (the 2-bit kernel fits 168 VGPRs),
+// and with more than 8 multi-query columns, whose longer pair path hides
+// better behind a third wave (168 VGPRs; its few spills sit outside the pair
+// loop). The launches size the grid to match (stream_waves).
+constexpr int waves_per_simd(int G, bool kMQ, int kBits) {
+  return (kBits == 2 || (kMQ && G > 8)) ? 3 : 2;
+}
 template <int G, bool kMQ, int kBits, bool kAppend>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kBits == 2 ? 3 : 2, kBits == 2 ? 3 : 2))) void decode_stream_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd(G, kMQ, kBits),
+                                                                     waves_per_simd(G, kMQ, kBits)))) void decode_stream_kernel(
     const __half* __restrict__ q, uint8_t* __restrict__ pages,
     __half* __restrict__ tail_k, __half* __restrict__ tail_v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
@@ -1536,6 +1543,12 @@ int resident_waves() {
   return cached;
 }
 
+namespace {
+// Grid of a decode stream launch whose kernel runs per_simd waves per SIMD
+// (resident_waves() counts two); the workspace holds slots for kMaxWaves.
+int stream_waves(int per_simd) { return std::min(resident_waves() / 2 * per_simd, kMaxWaves); }
+}  // namespace
+
 // Workspace: [total units, padded to 256 B] [first / last wave per (b, h),
 // padded to 256 B] [partial slots].
 namespace {
@@ -1623,10 +1636,8 @@ hipError_t launch_paged_decode(const s4kv_shape& s, const void* q, const void* p
                                int32_t max_ctx, float sm_scale, void* out, void* workspace,
                                hipStream_t stream, int bits) {
   const SplitWorkspace ws = split_workspace(s, workspace);
-  // 2-bit: three waves per SIMD (resident_waves() counts two); the workspace
-  // holds slots for kMaxWaves waves
-  const int W = (bits == 2) ? std::min(resident_waves() / 2 * 3, kMaxWaves) : resident_waves();
   const int G = s.num_q_heads / s.num_kv_heads;
+  const int W = stream_waves(waves_per_simd(G, false, bits));
   const hipError_t e =
       (bits == 2)
           ? launch_columns<false, 2>(G, s, W, q, pages, tail_k, tail_v, block_table, ctx_lens,
@@ -1664,7 +1675,7 @@ hipError_t launch_paged_mq(const s4kv_shape& s, const void* q, const int32_t* cu
   s4kv_shape sv = s;
   sv.num_seqs = static_cast<int32_t>(t.virtual_seqs);
   const SplitWorkspace ws = split_workspace(sv, workspace);
-  const int W = resident_waves();
+  const int W = stream_waves(waves_per_simd(t.columns, true, 4));
   const int gq = s.num_q_heads / s.num_kv_heads;
   const hipError_t e = launch_columns<true, 4>(
       t.columns, sv, W, q, pages, tail_k, tail_v, block_table, ctx_lens, ws.total_units,
