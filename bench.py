@@ -463,6 +463,40 @@ def read_ceiling(reps=10):
     return out
 
 
+def graph_call_ms(fns, reps=10, rounds=6):
+    """Per-call GPU time of each callable in `fns` ({name: launch one call}):
+    `reps` consecutive calls captured in one HIP graph per name, the graphs
+    replayed in turn `rounds` times (order alternating), each replay between
+    two events on the current stream; the median over replays, divided by
+    `reps`. This is the device time of the call without host launch gaps,
+    as the headline's graph-replayed steps measure it."""
+    import torch
+    graphs = {}
+    for name, fn in fns.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        graphs[name] = g
+    torch.cuda.synchronize()
+    for g in graphs.values():  # one untimed replay each
+        g.replay()
+    torch.cuda.synchronize()
+    ev = {name: [] for name in fns}
+    names = list(fns)
+    for r in range(rounds):
+        for name in (names if r % 2 == 0 else names[::-1]):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            graphs[name].replay()
+            b.record()
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    res = {name: float(np.median([a.elapsed_time(b) for a, b in ev[name]])) / reps for name in fns}
+    del graphs
+    return res
+
+
 def format_comparison(wl, calls=20, warmup=3):
     """The same decode over the four caches of this library on one layer of
     the workload: layer 0's cache built as int4 (s4kv_quantize_append), as
@@ -470,8 +504,10 @@ def format_comparison(wl, calls=20, warmup=3):
     control path) and as FP8 E4M3
     (s4kv_fp8_append, per-KV-head scales calibrated on sequence 0: its
     largest magnitude over 448); then `calls` decode calls of each,
-    interleaved, each timed with HIP events on the call's stream; medians are
-    reported, with each format's algorithmic bytes per call."""
+    interleaved, each timed with HIP events on the call's stream (medians,
+    `eager_call_ms`), and the same calls replayed from HIP graphs
+    (graph_call_ms: `call_ms`, the device time of a call, which the rates and
+    ratios use), with each format's algorithmic bytes per call."""
     import torch
     from int4_kivi_quantized_amd import Shape
     from int4_kivi_quantized_amd.cache import Fp8LayerCache, Fp16LayerCache, Kivi2LayerCache, LayerCache
@@ -517,21 +553,28 @@ def format_comparison(wl, calls=20, warmup=3):
             cache.decode(q, bt, ctx_g, max_ctx, out=outs[name])
             b.record()
     torch.cuda.synchronize()
-    res = {name: float(np.median([a.elapsed_time(b) for a, b in ev[name]])) for name in caches}
+    eager = {name: float(np.median([a.elapsed_time(b) for a, b in ev[name]])) for name in caches}
+    res = graph_call_ms({name: (lambda c=cache, o=outs[name]: c.decode(q, bt, ctx_g, max_ctx, out=o))
+                         for name, cache in caches.items()})
     del caches, outs
     torch.cuda.empty_cache()
     nbytes = {"int4": A.decode_bytes(ctx, wl.hq, wl.hkv),
               "kivi2": A.decode_bytes(ctx, wl.hq, wl.hkv, A.K2_CHUNK_BYTES),
               "fp16": A.fp16_decode_bytes(ctx, wl.hq, wl.hkv),
               "fp8": A.fp8_decode_bytes(ctx, wl.hq, wl.hkv)}
-    out = {"workload": f"{wl.name}, layer 0 (no append)", "calls": calls}
+    out = {"workload": f"{wl.name}, layer 0 (no append)", "calls": calls,
+           "timing": "call_ms: graph-replayed (10 calls per graph, median of 6 replays); "
+                     "eager_call_ms: eager launches between HIP events, median"}
     for name in ("int4", "kivi2", "fp16", "fp8"):
         gbs = nbytes[name] / (res[name] * 1e-3) / 1e9
-        out[name] = {"call_ms": round(res[name], 5), "bytes_per_call": nbytes[name],
+        out[name] = {"call_ms": round(res[name], 5), "eager_call_ms": round(eager[name], 5),
+                     "bytes_per_call": nbytes[name],
                      "gbs": round(gbs, 2), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4)}
     out["int4_speedup_over_fp16"] = round(res["fp16"] / res["int4"], 4)
     out["int4_speedup_over_fp8"] = round(res["fp8"] / res["int4"], 4)
     out["kivi2_speedup_over_int4"] = round(res["int4"] / res["kivi2"], 4)
+    out["kivi2_over_int4_time"] = round(res["kivi2"] / res["int4"], 4)
+    out["kivi2_over_int4_time_eager"] = round(eager["kivi2"] / eager["int4"], 4)
     return out
 
 
@@ -539,7 +582,8 @@ def multiquery_leg(wl, max_q=4, calls=20, warmup=3):
     """Multi-query attention (speculative verify: max_q new tokens per
     sequence, already appended) against the one-token decode call, on layer 0
     of the workload's int4 cache: `calls` calls of each, interleaved, HIP-event
-    medians."""
+    medians (eager), and the same calls replayed from HIP graphs
+    (graph_call_ms), which the reported call times and ratio use."""
     import torch
     from int4_kivi_quantized_amd import Shape
     from int4_kivi_quantized_amd.cache import LayerCache
@@ -581,7 +625,8 @@ def multiquery_leg(wl, max_q=4, calls=20, warmup=3):
             f()
             b.record()
     torch.cuda.synchronize()
-    ms = {k: float(np.median([a.elapsed_time(b) for a, b in ev[k]])) for k in run}
+    eager = {k: float(np.median([a.elapsed_time(b) for a, b in ev[k]])) for k in run}
+    ms = graph_call_ms(run)
     del cache, qm, outm, out1
     torch.cuda.empty_cache()
     mq_b = A.mq_bytes(ctx, t_counts, wl.hq, wl.hkv)
@@ -594,6 +639,11 @@ def multiquery_leg(wl, max_q=4, calls=20, warmup=3):
         "mq_query_tokens_per_s": round(int(t_counts.sum()) / (ms["mq"] * 1e-3), 1),
         "decode_call_ms": round(ms["decode"], 5),
         "mq_over_decode_time": round(ms["mq"] / ms["decode"], 4),
+        "timing": "call times graph-replayed (10 calls per graph, median of 6 replays); "
+                  "eager_*: eager launches between HIP events, median",
+        "eager_mq_call_ms": round(eager["mq"], 5),
+        "eager_decode_call_ms": round(eager["decode"], 5),
+        "mq_over_decode_time_eager": round(eager["mq"] / eager["decode"], 4),
     }
 
 
