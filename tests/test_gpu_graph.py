@@ -1,4 +1,4 @@
-"""The append and decode calls under HIP graph capture (torch.cuda.graph).
+"""The append, decode and multi-query calls under HIP graph capture (torch.cuda.graph).
 
 The C ABI allocates nothing and never synchronizes, so one decode step (append
 one token per sequence, then decode) can be captured once and replayed: each
@@ -118,3 +118,73 @@ def test_captured_fused_step_replays_match_eager():
         assert torch.equal(graph.cache.pages, eager.cache.pages), f"replay {s}: pages differ"
         assert torch.equal(graph.cache.tail_k, eager.cache.tail_k), f"replay {s}: tail K differs"
         assert torch.equal(graph.cache.tail_v, eager.cache.tail_v), f"replay {s}: tail V differs"
+
+
+@pytest.mark.parametrize("max_q", [4, 12])
+def test_captured_multiquery_replays_match_eager(max_q):
+    """s4kv_paged_attention_mq captured once and replayed with new query values
+    written in place between replays (eager work and synchronizations in
+    between): every replay equals the same call made eagerly. With 3 query
+    heads per KV head, 4 tokens fit one column tile (12 columns, the wide
+    layout) and 12 tokens take three tiles per sequence."""
+    print(f"[case] captured_multiquery max_q={max_q}", flush=True)
+    base = W.WORKLOADS["llama3.2-3b-layer"]
+    wl = W.Workload("graph-mq-3b", 1, 16, base.hq, base.hkv, base.ctx, base.k_outliers, seed=base.seed)
+    case = LayerCase(wl)
+    case.prefill()
+    t_counts = np.minimum(np.array([max_q - (b % 3) for b in range(wl.batch)]), case.ctx)
+    cu_q = torch.from_numpy(np.concatenate([[0], np.cumsum(t_counts)]).astype(np.int32)).cuda()
+    total_q = int(t_counts.sum())
+    max_ctx = int(case.ctx.max())
+    q_in = torch.empty((total_q, wl.hq, wl.head_dim), dtype=torch.float16, device="cuda")
+    out = torch.empty_like(q_in)
+    q_in.copy_(W.normal_fp16((total_q, wl.hq, wl.head_dim), 900, "cuda"))
+    case.cache.attend(q_in, cu_q, max_q, case.block_table, case.ctx_gpu, max_ctx, out=out)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        case.cache.attend(q_in, cu_q, max_q, case.block_table, case.ctx_gpu, max_ctx, out=out)
+    torch.cuda.synchronize()
+    for s in range(4):
+        q = W.normal_fp16((total_q, wl.hq, wl.head_dim), 901 + s, "cuda")
+        q_in.copy_(q)
+        g.replay()
+        junk = torch.randn(1 << 16, device="cuda").sum()          # unrelated eager work
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = case.cache.attend(q.contiguous(), cu_q, max_q, case.block_table, case.ctx_gpu, max_ctx)
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(got, ref), f"replay {s}: output differs from the eager call"
+
+
+def test_captured_fp16_decode_replays_match_eager():
+    """The fp16 control decode captured once and replayed with new queries
+    written in place: every replay equals the eager call."""
+    print("[case] captured_fp16_decode", flush=True)
+    base = W.WORKLOADS["llama3.2-3b-layer"]
+    wl = W.Workload("graph-fp16-3b", 1, 16, base.hq, base.hkv, base.ctx, base.k_outliers, seed=base.seed)
+    case = LayerCase(wl, kind="fp16")
+    case.prefill()
+    max_ctx = int(case.ctx.max())
+    q_in = torch.empty_like(case.q)
+    q_in.copy_(case.q)
+    out = torch.empty_like(case.q)
+    case.cache.decode(q_in, case.block_table, case.ctx_gpu, max_ctx, out=out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        case.cache.decode(q_in, case.block_table, case.ctx_gpu, max_ctx, out=out)
+    torch.cuda.synchronize()
+    for s in range(4):
+        q = W.normal_fp16(tuple(case.q.shape), 950 + s, "cuda")
+        q_in.copy_(q)
+        g.replay()
+        junk = torch.randn(1 << 16, device="cuda").sum()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = case.cache.decode(q.contiguous(), case.block_table, case.ctx_gpu, max_ctx)
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(got, ref), f"replay {s}: output differs from the eager call"
