@@ -422,6 +422,42 @@ s4kv_status s4kv_fp8_paged_decode(const s4kv_shape* shape, const void* q, const 
                                   const float* v_scale, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* ---- Table checks (a debugging aid) ----
+ *
+ * The append and decode kernels trust the device preconditions stated above
+ * for the block table and the context lengths (checking them in every page
+ * step would cost the hot path). This call checks them on the device, on
+ * demand, for callers that want to validate their tables before a call, in
+ * a debug build of their own code or in tests. It reads block_table and
+ * ctx_lens only within the shape's bounds and changes nothing else.
+ *
+ * For every sequence b it checks that 0 <= ctx_lens[b] <= 16 *
+ * max_pages_per_seq (a negative length, which the calls treat as an empty
+ * sequence, counts as a fault here) and, when max_ctx > 0, ctx_lens[b] <=
+ * max_ctx; and for
+ * every page p that holds one of the sequence's tokens, p < ceil(ctx_lens[b]
+ * / 16) (the pages of its first min(ctx_lens[b], 16 * max_pages_per_seq)
+ * tokens, the partial last page included, which an append completes), that
+ * 0 <= block_table[b][p] < num_pages.
+ *
+ * Args (device pointers unless noted):
+ *   block_table  int32 [B][max_pages_per_seq].
+ *   ctx_lens     int32 [B].
+ *   max_ctx      host int: the bound the next call will pass, or 0 to skip
+ *                that comparison.
+ *   report       int32 [4], written: [0] the sequences whose length is out of
+ *                range; [1] the block-table entries in use that are out of
+ *                range; [2] the smallest b with either fault, or -1; [3] that
+ *                sequence's first out-of-range page, or -1 when only its
+ *                length is out of range (or there is no fault).
+ * One launch of one work-group; stream-ordered like every other call.
+ * Returns S4KV_OK; S4KV_ERR_INVALID_ARG / S4KV_ERR_UNSUPPORTED before any
+ * launch (null pointers, max_ctx < 0, invalid shape); S4KV_ERR_HIP if the
+ * launch fails. */
+s4kv_status s4kv_check_tables(const s4kv_shape* shape, const int32_t* block_table,
+                              const int32_t* ctx_lens, int32_t max_ctx, int32_t* report,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

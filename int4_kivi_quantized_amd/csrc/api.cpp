@@ -76,6 +76,17 @@ s4kv_status s4kv_quantize_append(const s4kv_shape* shape, const void* k, const v
   return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
 }
 
+s4kv_status s4kv_check_tables(const s4kv_shape* shape, const int32_t* block_table,
+                              const int32_t* ctx_lens, int32_t max_ctx, int32_t* report,
+                              void* stream) {
+  const s4kv_status st = check_shape(shape);
+  if (st != S4KV_OK) return st;
+  if (!block_table || !ctx_lens || !report || max_ctx < 0) return S4KV_ERR_INVALID_ARG;
+  const hipError_t e = s4kv::launch_check_tables(*shape, block_table, ctx_lens, max_ctx, report,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? S4KV_OK : S4KV_ERR_HIP;
+}
+
 size_t s4kv_decode_workspace_bytes(const s4kv_shape* shape, int32_t max_ctx) {
   if (check_shape(shape) != S4KV_OK || max_ctx < 1) return 0;
   return s4kv::workspace_bytes(*shape);

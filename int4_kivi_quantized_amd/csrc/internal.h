@@ -137,4 +137,9 @@ hipError_t launch_fp8_decode(const s4kv_shape& s, const void* q, const void* pag
                              float sm_scale, const float* k_scale, const float* v_scale, void* out,
                              void* workspace, hipStream_t stream);
 
+// Table checks (check_tables.hip): report int32 [4] as s4kv_check_tables.
+hipError_t launch_check_tables(const s4kv_shape& s, const int32_t* block_table,
+                               const int32_t* ctx_lens, int32_t max_ctx, int32_t* report,
+                               hipStream_t stream);
+
 }  // namespace s4kv

@@ -133,6 +133,8 @@ def load():
     lib.s4kv_paged_attention_mq.argtypes = [SP, P, P, I32, I32, P, P, P, P, P, I32, ctypes.c_float,
                                             P, P, ctypes.c_size_t, P]
     lib.s4kv_paged_attention_mq.restype = ctypes.c_int
+    lib.s4kv_check_tables.argtypes = [SP, P, P, I32, P, P]
+    lib.s4kv_check_tables.restype = ctypes.c_int
     lib.s4kv_probe_read.argtypes = [P, ctypes.c_size_t, P, I32, I32, I32, P]
     lib.s4kv_probe_read.restype = ctypes.c_int
     _lib = lib
@@ -147,7 +149,7 @@ EXPORTED = (
     "s4kv_fp8_pool_bytes", "s4kv_fp8_append", "s4kv_fp8_paged_decode",
     "s4kv_mq_workspace_bytes", "s4kv_paged_attention_mq",
     "s4kv_kivi2_pool_bytes", "s4kv_kivi2_quantize_append", "s4kv_kivi2_paged_decode",
-    "s4kv_probe_read",
+    "s4kv_check_tables", "s4kv_probe_read",
 )
 
 
@@ -338,6 +340,19 @@ def s4kv_paged_attention_mq(shape, q, cu_q, max_q, pages, tail_k, tail_v, block_
         int(max_ctx), float(sm_scale), _ptr(out, torch.float16, "out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "s4kv_paged_attention_mq")
+
+
+def s4kv_check_tables(shape, block_table, ctx_lens, max_ctx, report, stream=None):
+    """Check block_table / ctx_lens against the shape on the device; report int32 [4] is
+    written (fault counts, first faulty sequence and page); see s4kv.h."""
+    import torch
+    _check_tables(shape, block_table, ctx_lens)
+    _numel(report, 4, "report")
+    st = load().s4kv_check_tables(
+        ctypes.byref(shape.c()), _ptr(block_table, torch.int32, "block_table"),
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), int(max_ctx), _ptr(report, torch.int32, "report"),
+        _stream(stream))
+    _check(st, "s4kv_check_tables")
 
 
 def s4kv_fp16_pool_bytes(shape):

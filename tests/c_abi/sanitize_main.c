@@ -51,7 +51,9 @@ int main(void) {
   CHECK(s4kv_fp8_paged_decode(&s, P, P, IP, IP, 1000, 0.088f, FP, FP, P, P, ws, NULL) == S4KV_OK);
   CHECK(s4kv_paged_decode_append_noalloc(&s, P, P, P, P, P, P, IP, IP, 1000, 0.088f, P, NULL) ==
         S4KV_OK);
-  CHECK(launched(n) == 11);
+  CHECK(s4kv_check_tables(&s, IP, IP, 1000, (int32_t*)P, NULL) == S4KV_OK);
+  CHECK(s4kv_check_tables(&s, IP, IP, 0, (int32_t*)P, NULL) == S4KV_OK);
+  CHECK(launched(n) == 13);
   /* max_new 0 appends nothing and launches nothing */
   n = stub_launches();
   CHECK(s4kv_quantize_append(&s, P, P, IP, IP, 0, IP, P, P, P, NULL) == S4KV_OK);
@@ -85,6 +87,10 @@ int main(void) {
   CHECK(s4kv_fp16_paged_decode(&s, P, P, IP, IP, 1000, 0.088f, P, P, 0, NULL) == S4KV_ERR_WORKSPACE);
   CHECK(s4kv_paged_decode_append_noalloc(&s, NULL, P, P, P, P, P, IP, IP, 1000, 0.088f, P, NULL) ==
         S4KV_ERR_INVALID_ARG);
+  CHECK(s4kv_check_tables(&s, NULL, IP, 1000, (int32_t*)P, NULL) == S4KV_ERR_INVALID_ARG);
+  CHECK(s4kv_check_tables(&s, IP, IP, 1000, NULL, NULL) == S4KV_ERR_INVALID_ARG);
+  CHECK(s4kv_check_tables(&s, IP, IP, -1, (int32_t*)P, NULL) == S4KV_ERR_INVALID_ARG);
+  CHECK(s4kv_check_tables(NULL, IP, IP, 1000, (int32_t*)P, NULL) == S4KV_ERR_INVALID_ARG);
   {
     /* a shape whose workspace exceeds the static scratch array */
     const s4kv_shape wide = {65535, 16, 16, S4KV_HEAD_DIM, S4KV_PAGE_SIZE, 100, 64};
