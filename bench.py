@@ -463,7 +463,7 @@ def read_ceiling(reps=10):
     return out
 
 
-def graph_call_ms(fns, reps=10, rounds=6):
+def graph_call_ms(fns, reps=10, rounds=15):
     """Per-call GPU time of each callable in `fns` ({name: launch one call}):
     `reps` consecutive calls captured in one HIP graph per name, the graphs
     replayed in turn `rounds` times (order alternating), each replay between
@@ -563,7 +563,7 @@ def format_comparison(wl, calls=20, warmup=3):
               "fp16": A.fp16_decode_bytes(ctx, wl.hq, wl.hkv),
               "fp8": A.fp8_decode_bytes(ctx, wl.hq, wl.hkv)}
     out = {"workload": f"{wl.name}, layer 0 (no append)", "calls": calls,
-           "timing": "call_ms: graph-replayed (10 calls per graph, median of 6 replays); "
+           "timing": "call_ms: graph-replayed (10 calls per graph, median of 15 replays); "
                      "eager_call_ms: eager launches between HIP events, median"}
     for name in ("int4", "kivi2", "fp16", "fp8"):
         gbs = nbytes[name] / (res[name] * 1e-3) / 1e9
@@ -639,7 +639,7 @@ def multiquery_leg(wl, max_q=4, calls=20, warmup=3):
         "mq_query_tokens_per_s": round(int(t_counts.sum()) / (ms["mq"] * 1e-3), 1),
         "decode_call_ms": round(ms["decode"], 5),
         "mq_over_decode_time": round(ms["mq"] / ms["decode"], 4),
-        "timing": "call times graph-replayed (10 calls per graph, median of 6 replays); "
+        "timing": "call times graph-replayed (10 calls per graph, median of 15 replays); "
                   "eager_*: eager launches between HIP events, median",
         "eager_mq_call_ms": round(eager["mq"], 5),
         "eager_decode_call_ms": round(eager["decode"], 5),
