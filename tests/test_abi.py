@@ -316,3 +316,20 @@ def test_mq_workspace_and_refusals():
     assert call(shape=Shape(**{**GOOD, "page_size": 8}).c()) == s4kv.S4KV_ERR_UNSUPPORTED
     for i in range(9):
         assert call(null_at=i) == s4kv.S4KV_ERR_INVALID_ARG
+
+
+def test_check_tables_refuses_before_launch():
+    lib, P, fake = _raw_calls()
+    good = Shape(**GOOD).c()
+    bad = Shape(**{**GOOD, "num_q_heads": 12}).c()
+    assert lib.s4kv_check_tables(ctypes.byref(bad), fake, fake, 0, fake, None) == \
+        s4kv.S4KV_ERR_UNSUPPORTED
+    assert lib.s4kv_check_tables(None, fake, fake, 0, fake, None) == s4kv.S4KV_ERR_INVALID_ARG
+    assert lib.s4kv_check_tables(ctypes.byref(good), fake, fake, -1, fake, None) == \
+        s4kv.S4KV_ERR_INVALID_ARG
+    for null_at in range(3):
+        ptrs = [fake] * 3
+        ptrs[null_at] = None
+        bt, cl, rep = ptrs
+        assert lib.s4kv_check_tables(ctypes.byref(good), bt, cl, 1000, rep, None) == \
+            s4kv.S4KV_ERR_INVALID_ARG
